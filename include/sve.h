@@ -1,0 +1,199 @@
+/*
+ * sve.h — C ABI of libsve: extend-prefill attention over resident KV slots and
+ * the m-row int4 GEMV, for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions
+ *   - Every function returns 0 (SVE_OK) or a negative SVE_E_* code and never
+ *     throws. Arguments are checked on the host before anything is enqueued;
+ *     on error nothing is enqueued and no state changes.
+ *   - "device" pointers are HIP device memory owned by the caller (for example
+ *     torch tensors); the library never allocates, frees or retains them
+ *     beyond the call, except the arena handed to sve_create, which must stay
+ *     allocated until sve_destroy.
+ *   - "host" pointers are ordinary host memory, read during the call only.
+ *   - hip_stream is a hipStream_t (NULL = the legacy default stream). Work is
+ *     enqueued asynchronously on it unless a function says it synchronises.
+ *   - bf16 and fp16 values are passed as their 16-bit patterns.
+ *   - One context may be used by one host thread at a time.
+ *
+ * Source pages cited below:
+ *   [goinfer]  goinfer, "Turn nine in under half a second"
+ *   [spec]     thinkspread, "The economics of speculative decoding: +41% on
+ *              9B, break-even on 35B"
+ *   [quant]    thinkspread, "Models and quantizations"
+ */
+#ifndef SVE_H
+#define SVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SVE_OK = 0,
+  SVE_E_ARG = -1,      /* null pointer, bad size or shape */
+  SVE_E_SLOT = -2,     /* slot or layer index out of range */
+  SVE_E_CAPACITY = -3, /* more tokens or rows than the context was built for */
+  SVE_E_HIP = -4,      /* a HIP runtime call failed (text: sve_last_error) */
+  SVE_E_STATE = -5     /* call out of order, e.g. extend past the selected prompt */
+};
+
+#define SVE_MAX_SLOTS 4
+
+typedef struct sve_ctx sve_ctx;
+
+/* Shape of a KV-slot store. [goinfer] "How it works": a GPU-resident model
+ * keeps up to --kv-sessions KV slots, one conversation each; "Use it": the
+ * default is 4 and 0 switches reuse off. */
+typedef struct {
+  int32_t n_slots;    /* requested slots, 1..SVE_MAX_SLOTS */
+  int32_t n_layers;   /* KV layers held per slot, >= 1 */
+  int32_t n_q_heads;  /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads; /* Hkv */
+  int32_t head_dim;   /* D: 64 or 128 */
+  int32_t capacity;   /* max tokens per slot (rounded up to a multiple of 64) */
+  int32_t max_rows;   /* max new rows per extend call (sum over a batched call) */
+  int32_t reuse;      /* 0: select always reports 0 reused tokens */
+  int32_t match_rule; /* 0: lone-slot clause on (default); 1: literal rule */
+} sve_config;
+
+/* Bytes of device memory a context needs for `n_slots` slots: the KV store,
+ * the token mirrors, and the split-KV workspace. 0 if cfg is invalid. */
+size_t sve_arena_bytes(const sve_config* cfg, int32_t n_slots);
+
+/* Create a context over a caller-owned device arena of `arena_bytes` bytes
+ * (256-byte aligned). As many of the requested slots as fit are granted
+ * ([goinfer] "Use it": the memory check may grant fewer slots than asked,
+ * and both numbers are reported); *granted_slots receives that number.
+ * The arena is cleared on `hip_stream`. Errors: SVE_E_ARG (bad config, null
+ * pointers, misaligned arena), SVE_E_CAPACITY (not even one slot fits),
+ * SVE_E_HIP. */
+int sve_create(const sve_config* cfg, void* arena, size_t arena_bytes, void* hip_stream,
+               sve_ctx** out, int32_t* granted_slots);
+
+/* Free the host-side context. The arena stays the caller's. */
+int sve_destroy(sve_ctx* ctx);
+
+/* Use another stream for later calls on this context. */
+int sve_set_stream(sve_ctx* ctx, void* hip_stream);
+
+/* Pick the slot for a new prompt and report how many of its leading tokens
+ * are already cached ([goinfer] "How it works": longest common start, which
+ * must beat what that slot shares with the other slots; a GPU request reuses
+ * the slot holding the start of its prompt, else an empty slot, else the
+ * least recently used one; the conversation is cut back to the shared point
+ * and the reuse count reported to the caller).
+ *   tokens_host: host int32 [n], 1 <= n <= capacity.
+ *   *slot, *reused: the chosen slot and the reused prefix length r
+ *     (r <= n-1, so the last prompt token always runs through the model).
+ * Commits: the slot's prompt becomes `tokens`, every layer's cached length
+ * becomes r, the slot becomes most recently used. Only tokens whose K/V rows
+ * are cached in every layer take part in matching. A slot is eligible when
+ * its common start with the prompt is > 0, exceeds its common start with
+ * every other occupied slot, and either covers the whole slot or some other
+ * slot is occupied (match_rule 1 drops this last clause).
+ * SYNCHRONISES the context stream (one small device-to-host read).
+ * Errors: SVE_E_ARG, SVE_E_CAPACITY (n > capacity), SVE_E_HIP. */
+int sve_kv_slot_select(sve_ctx* ctx, const int32_t* tokens_host, int32_t n, int32_t* slot,
+                       int32_t* reused);
+
+/* Cut a slot back to `len` cached positions in every layer ([goinfer] "How it
+ * works": cut back to the shared point). Metadata only; the selected prompt
+ * is kept, so later extend calls may refill it. len must not exceed any
+ * layer's cached length. Errors: SVE_E_SLOT, SVE_E_ARG. */
+int sve_kv_truncate(sve_ctx* ctx, int32_t slot, int32_t len);
+
+/* Cached length of (slot, layer). */
+int sve_kv_len(const sve_ctx* ctx, int32_t slot, int32_t layer, int32_t* len);
+
+/* Granted slot count and padded per-slot capacity. */
+int sve_info(const sve_ctx* ctx, int32_t* granted_slots, int32_t* capacity);
+
+/* Extend-prefill: append m new rows to (slot, layer) and attend.
+ * With P the cached length, query row i (absolute position P+i) attends
+ * causally to positions 0..P+i of that slot and layer, with scores scaled by
+ * 1/sqrt(D) and q head h reading KV head h / (Hq/Hkv); q and k arrive
+ * position-encoded. ([goinfer] "What goinfer does": only the tokens after the
+ * reused start are prefilled against the kept KV cache; [spec] opening
+ * section: the k+1 verify rows are one such pass.)
+ *   q:     device bf16 [m][Hq][D]
+ *   new_k: device bf16 [m][Hkv][D]   (stored at positions P..P+m-1)
+ *   new_v: device bf16 [m][Hkv][D]
+ *   out:   device bf16 [m][Hq][D]    (fp32 accumulation, rounded to nearest even)
+ * m == 0 is a no-op. Asynchronous; the cached length becomes P+m.
+ * Errors: SVE_E_SLOT, SVE_E_ARG, SVE_E_CAPACITY (m > max_rows),
+ * SVE_E_STATE (P+m beyond the prompt committed by the last select), SVE_E_HIP. */
+int sve_extend_attn(sve_ctx* ctx, int32_t slot, int32_t layer, const void* q, const void* new_k,
+                    const void* new_v, int32_t m, void* out);
+
+/* The same for n distinct slots in one launch (rows packed slot after slot:
+ * q_packed [sum m][Hq][D], k_packed/v_packed [sum m][Hkv][D], out_packed
+ * [sum m][Hq][D]). slots_host, m_host: host int32 [n], 1 <= n <= 4.
+ * Errors as sve_extend_attn; SVE_E_ARG also for a repeated slot. */
+int sve_extend_attn_batched(sve_ctx* ctx, int32_t n, const int32_t* slots_host,
+                            const int32_t* m_host, int32_t layer, const void* q_packed,
+                            const void* k_packed, const void* v_packed, void* out_packed);
+
+/* Copy cached rows [start, start+len) of (slot, layer) to k_out, v_out:
+ * device bf16 [len][Hkv][D] each (test export). */
+int sve_kv_read(sve_ctx* ctx, int32_t slot, int32_t layer, int32_t start, int32_t len,
+                void* k_out, void* v_out);
+
+/* ---- int4 group-32 weights ([quant] "Quantizations": 32-element blocks with
+ * one scale, used in place) --------------------------------------------------
+ * Logical format: w uint8 [N][K/2], element k in the low nibble of byte k/2
+ * for even k and the high nibble for odd k; scales fp16 [N][K/32];
+ * value = (code - 8) * scale. The GEMV reads a device layout written once by
+ * sve_w4_pack (same byte count, rows padded to 16 and k to 128). */
+
+/* Bytes of the device layout of an N x K weight. 0 if N < 1 or K % 32. */
+size_t sve_w4_packed_bytes(int32_t N, int32_t K);
+
+/* Convert a logical weight (device w, device scales) into the device layout
+ * (device `packed`, sve_w4_packed_bytes(N, K) bytes). Errors: SVE_E_ARG, SVE_E_HIP. */
+int sve_w4_pack(const uint8_t* w, const uint16_t* scales, int32_t N, int32_t K, void* packed,
+                void* hip_stream);
+
+/* Decode a packed weight to device fp32 [N][K]; (code-8)*scale is exact in
+ * fp32 (test export). */
+int sve_w4_dequant(const void* packed, int32_t N, int32_t K, float* out, void* hip_stream);
+
+/* m-row GEMV: y[r][n] = sum_k x[r][k] * w[n][k], the weights read once for
+ * all m rows ([spec] opening section: verify rows share one read of the
+ * weights, so extra rows are nearly free).
+ *   x: device bf16 [m][K]; packed: sve_w4_pack output; y: device fp32 [m][N].
+ *   1 <= m <= 16, N >= 1, K % 32 == 0.
+ * Errors: SVE_E_ARG, SVE_E_HIP. */
+int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
+                  void* hip_stream);
+
+/* Expert-routed GEMV for a mixture-of-experts layer ([spec] "Architecture
+ * decides whether it pays": rows pick different experts, so expert weights
+ * are not shared across rows). Pair (r, j) computes
+ * y[r][j][:] = W_{ids[r][j]} x(r, j), where x(r, j) = x[r] (x_per_slot 0,
+ * x device bf16 [m][K]) or x[r][j] (x_per_slot 1, x [m][topk][K]). Each
+ * distinct expert's weights are read once for all pairs routed to it.
+ *   expert_ids: device int32 [m][topk]; packed_all: E packed weights of
+ *   sve_w4_packed_bytes(N, K) bytes each, back to back; y: device fp32
+ *   [m][topk][N]. 1 <= m <= 16, 1 <= topk <= 16. An id outside 0..E-1
+ *   yields NaN in that pair's output row.
+ * Errors: SVE_E_ARG, SVE_E_HIP. */
+int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int32_t* expert_ids,
+                         int32_t topk, const void* packed_all, int32_t E, int32_t N, int32_t K,
+                         float* y, void* hip_stream);
+
+/* Message for a status code. */
+const char* sve_strerror(int code);
+
+/* Text of the last error on this context, or of the calling thread's last
+ * error from a context-free call when ctx is NULL. */
+const char* sve_last_error(const sve_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVE_H */

@@ -1,0 +1,205 @@
+"""Extend-prefill attention over resident KV slots and the m-row int4 GEMV on
+AMD Instinct MI355X (gfx950).
+
+Thin torch-facing binding of libsve (include/sve.h): it checks tensor
+devices, dtypes and shapes, passes raw pointers and the current HIP stream,
+and nothing else. Every computation runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import SveError, check
+
+__all__ = ["KVSlots", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m",
+           "w4_gemv_m_routed", "SveError", "load_library"]
+
+
+def load_library():
+    """Load libsve.so (raises if it was not built)."""
+    return _lib.load()
+
+
+def _stream() -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> C.c_void_p:
+    return C.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, shape, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class KVSlots:
+    """A resident KV-slot store (up to four conversations) on one GPU."""
+
+    def __init__(self, n_slots: int, n_layers: int, n_q_heads: int, n_kv_heads: int,
+                 head_dim: int, capacity: int, max_rows: int, reuse: bool = True,
+                 match_rule: int = 0, device="cuda", arena_bytes: int | None = None):
+        lib = _lib.load()
+        self.cfg = _lib.SveConfig(n_slots, n_layers, n_q_heads, n_kv_heads, head_dim,
+                                  capacity, max_rows, int(bool(reuse)), match_rule)
+        need = lib.sve_arena_bytes(C.byref(self.cfg), n_slots)
+        if need == 0:
+            raise ValueError("invalid KV-slot configuration")
+        nbytes = need if arena_bytes is None else int(arena_bytes)
+        self.requested = n_slots
+        self.arena = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ctx = C.c_void_p()
+        granted = C.c_int32()
+        check(lib.sve_create(C.byref(self.cfg), _ptr(self.arena), nbytes, _stream(),
+                             C.byref(ctx), C.byref(granted)))
+        self._lib = lib
+        self.ctx = ctx
+        self.granted = granted.value
+        cap = C.c_int32()
+        check(lib.sve_info(ctx, C.byref(granted), C.byref(cap)), ctx)
+        self.capacity = cap.value
+        self.hq, self.hkv, self.d = n_q_heads, n_kv_heads, head_dim
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            self._lib.sve_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _bind(self) -> None:
+        check(self._lib.sve_set_stream(self.ctx, _stream()), self.ctx)
+
+    def kv_slot_select(self, tokens) -> tuple[int, int]:
+        """(slot, reused) for a prompt of token ids (host ints). Synchronises."""
+        self._bind()
+        arr = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        slot, reused = C.c_int32(), C.c_int32()
+        check(self._lib.sve_kv_slot_select(self.ctx, arr.ctypes.data_as(C.c_void_p), arr.size,
+                                           C.byref(slot), C.byref(reused)), self.ctx)
+        return slot.value, reused.value
+
+    def kv_truncate(self, slot: int, length: int) -> None:
+        check(self._lib.sve_kv_truncate(self.ctx, slot, length), self.ctx)
+
+    def kv_len(self, slot: int, layer: int = 0) -> int:
+        n = C.c_int32()
+        check(self._lib.sve_kv_len(self.ctx, slot, layer, C.byref(n)), self.ctx)
+        return n.value
+
+    def extend_attn(self, slot: int, layer: int, q: torch.Tensor, new_k: torch.Tensor,
+                    new_v: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Append m rows to (slot, layer) and attend; q [m][Hq][D] bf16,
+        new_k/new_v [m][Hkv][D] bf16; returns out [m][Hq][D] bf16."""
+        m = q.shape[0]
+        _need(q, torch.bfloat16, (m, self.hq, self.d), "q")
+        _need(new_k, torch.bfloat16, (m, self.hkv, self.d), "new_k")
+        _need(new_v, torch.bfloat16, (m, self.hkv, self.d), "new_v")
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, torch.bfloat16, (m, self.hq, self.d), "out")
+        self._bind()
+        check(self._lib.sve_extend_attn(self.ctx, slot, layer, _ptr(q), _ptr(new_k),
+                                        _ptr(new_v), m, _ptr(out)), self.ctx)
+        return out
+
+    def extend_attn_batched(self, slots, ms, layer: int, q: torch.Tensor, new_k: torch.Tensor,
+                            new_v: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """extend_attn over several slots in one launch; rows packed slot after slot."""
+        slots = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+        ms = np.ascontiguousarray(np.asarray(ms, dtype=np.int32))
+        total = int(ms.sum())
+        _need(q, torch.bfloat16, (total, self.hq, self.d), "q")
+        _need(new_k, torch.bfloat16, (total, self.hkv, self.d), "new_k")
+        _need(new_v, torch.bfloat16, (total, self.hkv, self.d), "new_v")
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, torch.bfloat16, (total, self.hq, self.d), "out")
+        self._bind()
+        check(self._lib.sve_extend_attn_batched(
+            self.ctx, len(slots), slots.ctypes.data_as(C.c_void_p),
+            ms.ctypes.data_as(C.c_void_p), layer, _ptr(q), _ptr(new_k), _ptr(new_v),
+            _ptr(out)), self.ctx)
+        return out
+
+    def kv_read(self, slot: int, layer: int, start: int, length: int):
+        """Cached K and V rows [start, start+length) as bf16 [length][Hkv][D]."""
+        k = torch.empty((length, self.hkv, self.d), dtype=torch.bfloat16, device=self.arena.device)
+        v = torch.empty_like(k)
+        self._bind()
+        check(self._lib.sve_kv_read(self.ctx, slot, layer, start, length, _ptr(k), _ptr(v)),
+              self.ctx)
+        return k, v
+
+
+def w4_packed_bytes(n: int, k: int) -> int:
+    return int(_lib.load().sve_w4_packed_bytes(n, k))
+
+
+def w4_pack(w: torch.Tensor, scales: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """Device layout of an int4 group-32 weight (w uint8 [N][K/2], scales
+    fp16 [N][K/32])."""
+    lib = _lib.load()
+    _need(w, torch.uint8, (n, k // 2), "w")
+    _need(scales, torch.float16, (n, k // 32), "scales")
+    nbytes = lib.sve_w4_packed_bytes(n, k)
+    if nbytes == 0:
+        raise ValueError("need N >= 1 and K % 32 == 0")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    check(lib.sve_w4_pack(_ptr(w), _ptr(scales), n, k, _ptr(packed), _stream()))
+    return packed
+
+
+def w4_dequant(packed: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    lib = _lib.load()
+    _need(packed, torch.uint8, (lib.sve_w4_packed_bytes(n, k),), "packed")
+    out = torch.empty((n, k), dtype=torch.float32, device=packed.device)
+    check(lib.sve_w4_dequant(_ptr(packed), n, k, _ptr(out), _stream()))
+    return out
+
+
+def w4_gemv_m(x: torch.Tensor, packed: torch.Tensor, n: int, k: int,
+              y: torch.Tensor | None = None) -> torch.Tensor:
+    """y [m][N] fp32 = x [m][K] bf16 times the packed int4 weight."""
+    lib = _lib.load()
+    m = x.shape[0]
+    _need(x, torch.bfloat16, (m, k), "x")
+    _need(packed, torch.uint8, (lib.sve_w4_packed_bytes(n, k),), "packed")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, (m, n), "y")
+    check(lib.sve_w4_gemv_m(_ptr(x), m, _ptr(packed), n, k, _ptr(y), _stream()))
+    return y
+
+
+def w4_gemv_m_routed(x: torch.Tensor, expert_ids: torch.Tensor, packed_all: torch.Tensor,
+                     n_experts: int, n: int, k: int, x_per_slot: bool = False,
+                     y: torch.Tensor | None = None) -> torch.Tensor:
+    """y [m][topk][N] fp32: each (row, expert slot) through its own expert."""
+    lib = _lib.load()
+    m, topk = expert_ids.shape
+    _need(expert_ids, torch.int32, (m, topk), "expert_ids")
+    _need(x, torch.bfloat16, (m, topk, k) if x_per_slot else (m, k), "x")
+    _need(packed_all, torch.uint8, (n_experts * lib.sve_w4_packed_bytes(n, k),), "packed_all")
+    if y is None:
+        y = torch.empty((m, topk, n), dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, (m, topk, n), "y")
+    check(lib.sve_w4_gemv_m_routed(_ptr(x), int(bool(x_per_slot)), m, _ptr(expert_ids), topk,
+                                   _ptr(packed_all), n_experts, n, k, _ptr(y), _stream()))
+    return y

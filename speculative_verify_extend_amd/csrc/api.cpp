@@ -1,0 +1,490 @@
+// libsve host side: the C ABI declared in include/sve.h.
+//
+// The context owns only host metadata (cached lengths, selected prompts'
+// lengths, LRU ticks). Device memory is the caller's arena:
+//   [prompt tokens: cap int32][slot token mirrors: 4 x cap int32][LCP out]
+//   [split workspace: partial O fp32, (max, sum) fp32][slot 0][slot 1]...
+// and each slot holds n_layers x { K [Hkv][cap][D], Vt [Hkv][D][cap] } bf16.
+#include "sve.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+using namespace sve;
+
+namespace {
+
+constexpr int kMaxSplits = 16;
+constexpr size_t kAlign = 256;
+thread_local std::string g_err;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  int cap;
+  size_t off_tok, off_slot_tok, off_lcp, off_ws_o, off_ws_ml, fixed, layer_bytes, slot_bytes;
+};
+
+bool config_ok(const sve_config* c, std::string* why) {
+  if (!c) return *why = "null config", false;
+  if (c->n_slots < 1 || c->n_slots > SVE_MAX_SLOTS) return *why = "n_slots must be 1..4", false;
+  if (c->n_layers < 1) return *why = "n_layers must be >= 1", false;
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads)
+    return *why = "n_q_heads must be a positive multiple of n_kv_heads", false;
+  if (c->head_dim != 64 && c->head_dim != 128) return *why = "head_dim must be 64 or 128", false;
+  if (c->capacity < 1 || c->capacity > (1 << 20)) return *why = "capacity out of range", false;
+  if (c->max_rows < 1 || c->max_rows > c->capacity)
+    return *why = "max_rows must be 1..capacity", false;
+  if (c->match_rule != 0 && c->match_rule != 1) return *why = "match_rule must be 0 or 1", false;
+  return true;
+}
+
+Layout make_layout(const sve_config* c) {
+  Layout L;
+  L.cap = (c->capacity + 63) / 64 * 64;
+  size_t off = 0;
+  L.off_tok = off;
+  off += align_up((size_t)L.cap * 4);
+  L.off_slot_tok = off;
+  off += align_up((size_t)SVE_MAX_SLOTS * L.cap * 4);
+  L.off_lcp = off;
+  off += align_up((size_t)kMaxLcpPairs * 4);
+  L.off_ws_o = off;
+  off += align_up((size_t)kMaxSplits * c->max_rows * c->n_q_heads * c->head_dim * 4);
+  L.off_ws_ml = off;
+  off += align_up((size_t)kMaxSplits * c->max_rows * c->n_q_heads * 2 * 4);
+  L.fixed = off;
+  L.layer_bytes = align_up((size_t)2 * c->n_kv_heads * L.cap * c->head_dim * 2);
+  L.slot_bytes = (size_t)c->n_layers * L.layer_bytes;
+  return L;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+bool log_on() { return env_int("SVE_LOG", 0) != 0; }
+
+}  // namespace
+
+struct sve_ctx {
+  sve_config cfg;
+  Layout lay;
+  int granted;
+  hipStream_t stream;
+  uint8_t* arena;
+  size_t arena_bytes;
+  std::vector<std::vector<int>> kv_len;  // [slot][layer]
+  std::vector<int> committed;            // length of the prompt selected into the slot
+  std::vector<long long> tick;
+  long long clock;
+  std::string err;
+
+  int32_t* tok() { return (int32_t*)(arena + lay.off_tok); }
+  int32_t* slot_tok(int s) { return (int32_t*)(arena + lay.off_slot_tok) + (size_t)s * lay.cap; }
+  int32_t* lcp_out() { return (int32_t*)(arena + lay.off_lcp); }
+  float* ws_o() { return (float*)(arena + lay.off_ws_o); }
+  float* ws_ml() { return (float*)(arena + lay.off_ws_ml); }
+  uint16_t* kbase(int s, int l) {
+    return (uint16_t*)(arena + lay.fixed + (size_t)s * lay.slot_bytes + (size_t)l * lay.layer_bytes);
+  }
+  uint16_t* vtbase(int s, int l) {
+    return kbase(s, l) + (size_t)cfg.n_kv_heads * lay.cap * cfg.head_dim;
+  }
+  int resident(int s) const {
+    int r = kv_len[s][0];
+    for (int v : kv_len[s]) r = std::min(r, v);
+    return r;
+  }
+};
+
+namespace {
+
+int fail(const sve_ctx* c, int code, const std::string& msg) {
+  if (c)
+    const_cast<sve_ctx*>(c)->err = msg;
+  else
+    g_err = msg;
+  return code;
+}
+
+int hip_fail(const sve_ctx* c, hipError_t e, const char* what) {
+  return fail(c, SVE_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define SVE_HIP(ctx, expr)                                 \
+  do {                                                     \
+    hipError_t e_ = (expr);                                \
+    if (e_ != hipSuccess) return hip_fail(ctx, e_, #expr); \
+  } while (0)
+
+// Choose the path, row blocks and key splits of every piece of a call.
+void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
+  const int g = p.g;
+  int max_m = 0;
+  for (int s = 0; s < p.nseg; ++s) max_m = std::max(max_m, p.seg[s].m);
+  const int mfma_min = env_int("SVE_MFMA_MIN_ROWS", 16);
+  path = (max_m >= mfma_min) ? kPathMfma : kPathValu;
+  const int rpb = attn_rows_per_block(path);
+  int base = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    p.seg[s].row_blocks = (p.seg[s].m * g + rpb - 1) / rpb;
+    base += p.Hkv * p.seg[s].row_blocks;
+  }
+  const int target = path == kPathValu ? 512 : 256;
+  const int forced = env_int("SVE_KV_SPLIT", 0);
+  int blocks = 0, rows = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    AttnSeg& sg = p.seg[s];
+    const int keys = sg.P + sg.m;
+    int S = forced > 0 ? forced : (target + base - 1) / std::max(base, 1);
+    S = std::max(1, std::min(S, kMaxSplits));
+    S = std::min(S, (keys + 63) / 64);
+    int sk = (keys + S - 1) / S;
+    sk = (sk + 63) / 64 * 64;
+    S = (keys + sk - 1) / sk;
+    sg.splits = S;
+    sg.split_keys = sk;
+    sg.block_begin = blocks;
+    sg.row_begin = rows;
+    sg.ws_o = c->ws_o() + (size_t)rows * kMaxSplits * p.Hq * p.D;
+    sg.ws_ml = c->ws_ml() + (size_t)rows * kMaxSplits * p.Hq * 2;
+    blocks += p.Hkv * sg.row_blocks * S;
+    rows += sg.m;
+  }
+  p.total_blocks = blocks;
+  p.total_rows = rows;
+  if (log_on()) {
+    fprintf(stderr, "[sve] extend: path=%s pieces=%d blocks=%d", path == kPathMfma ? "mfma" : "valu",
+            p.nseg, blocks);
+    for (int s = 0; s < p.nseg; ++s)
+      fprintf(stderr, " (P=%d m=%d splits=%d x %d keys)", p.seg[s].P, p.seg[s].m, p.seg[s].splits,
+              p.seg[s].split_keys);
+    fprintf(stderr, "\n");
+  }
+}
+
+int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int layer,
+               const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out) {
+  const sve_config& cf = c->cfg;
+  if (n < 1 || n > kMaxSeg) return fail(c, SVE_E_ARG, "batched extend takes 1..4 slots");
+  if (layer < 0 || layer >= cf.n_layers) return fail(c, SVE_E_SLOT, "layer out of range");
+  int total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= c->granted) return fail(c, SVE_E_SLOT, "slot out of range");
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == slots[i]) return fail(c, SVE_E_ARG, "a slot appears twice in one call");
+    if (ms[i] < 0) return fail(c, SVE_E_ARG, "m must be >= 0");
+    const int P = c->kv_len[slots[i]][layer];
+    if (P + ms[i] > c->committed[slots[i]])
+      return fail(c, SVE_E_STATE, "extend past the prompt committed by the last select");
+    total += ms[i];
+  }
+  if (total > cf.max_rows) return fail(c, SVE_E_CAPACITY, "more rows than max_rows");
+  if (total == 0) return SVE_OK;
+  if (!q || !k || !v || !out) return fail(c, SVE_E_ARG, "null tensor pointer");
+
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.Hq = cf.n_q_heads;
+  p.Hkv = cf.n_kv_heads;
+  p.g = p.Hq / p.Hkv;
+  p.D = cf.head_dim;
+  p.cap = c->lay.cap;
+  p.c = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+  int row = 0;
+  for (int i = 0; i < n; ++i) {
+    if (ms[i] == 0) continue;
+    AttnSeg& sg = p.seg[p.nseg++];
+    sg.K = c->kbase(slots[i], layer);
+    sg.Vt = c->vtbase(slots[i], layer);
+    sg.q = q + (size_t)row * p.Hq * p.D;
+    sg.nk = k + (size_t)row * p.Hkv * p.D;
+    sg.nv = v + (size_t)row * p.Hkv * p.D;
+    sg.out = out + (size_t)row * p.Hq * p.D;
+    sg.P = c->kv_len[slots[i]][layer];
+    sg.m = ms[i];
+    row += ms[i];
+  }
+  int path = kPathMfma;
+  plan_attention(c, p, path);
+  hipError_t e = launch_kv_append(p, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "kv_append launch");
+  e = launch_attn(p, path, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "extend_attn launch");
+  e = launch_attn_combine(p, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "combine launch");
+  for (int i = 0; i < n; ++i) c->kv_len[slots[i]][layer] += ms[i];
+  return SVE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sve_arena_bytes(const sve_config* cfg, int32_t n_slots) {
+  std::string why;
+  if (!config_ok(cfg, &why) || n_slots < 1 || n_slots > SVE_MAX_SLOTS) return 0;
+  const Layout L = make_layout(cfg);
+  return L.fixed + (size_t)n_slots * L.slot_bytes;
+}
+
+int sve_create(const sve_config* cfg, void* arena, size_t arena_bytes, void* hip_stream,
+               sve_ctx** out, int32_t* granted_slots) {
+  std::string why;
+  if (!config_ok(cfg, &why)) return fail(nullptr, SVE_E_ARG, why);
+  if (!arena || !out || !granted_slots) return fail(nullptr, SVE_E_ARG, "null pointer");
+  if ((uintptr_t)arena % kAlign) return fail(nullptr, SVE_E_ARG, "arena must be 256-byte aligned");
+  const Layout L = make_layout(cfg);
+  if (arena_bytes < L.fixed + L.slot_bytes)
+    return fail(nullptr, SVE_E_CAPACITY, "arena too small for one slot");
+  const int granted =
+      (int)std::min<size_t>((size_t)cfg->n_slots, (arena_bytes - L.fixed) / L.slot_bytes);
+  sve_ctx* c = new sve_ctx();
+  c->cfg = *cfg;
+  c->lay = L;
+  c->granted = granted;
+  c->stream = (hipStream_t)hip_stream;
+  c->arena = (uint8_t*)arena;
+  c->arena_bytes = arena_bytes;
+  c->kv_len.assign(granted, std::vector<int>(cfg->n_layers, 0));
+  c->committed.assign(granted, 0);
+  c->tick.assign(granted, 0);
+  c->clock = 0;
+  hipError_t e = hipMemsetAsync(arena, 0, L.fixed + (size_t)granted * L.slot_bytes, c->stream);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(nullptr, e, "hipMemsetAsync(arena)");
+  }
+  if (log_on())
+    fprintf(stderr, "[sve] slots requested %d, granted %d (cap %d, %zu bytes per slot)\n",
+            cfg->n_slots, granted, L.cap, L.slot_bytes);
+  *out = c;
+  *granted_slots = granted;
+  return SVE_OK;
+}
+
+int sve_destroy(sve_ctx* ctx) {
+  if (!ctx) return fail(nullptr, SVE_E_ARG, "null context");
+  delete ctx;
+  return SVE_OK;
+}
+
+int sve_set_stream(sve_ctx* ctx, void* hip_stream) {
+  if (!ctx) return fail(nullptr, SVE_E_ARG, "null context");
+  ctx->stream = (hipStream_t)hip_stream;
+  return SVE_OK;
+}
+
+int sve_info(const sve_ctx* ctx, int32_t* granted_slots, int32_t* capacity) {
+  if (!ctx || !granted_slots || !capacity) return fail(ctx, SVE_E_ARG, "null pointer");
+  *granted_slots = ctx->granted;
+  *capacity = ctx->lay.cap;
+  return SVE_OK;
+}
+
+int sve_kv_slot_select(sve_ctx* c, const int32_t* tokens, int32_t n, int32_t* slot,
+                       int32_t* reused) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  if (!tokens || !slot || !reused) return fail(c, SVE_E_ARG, "null pointer");
+  if (n < 1) return fail(c, SVE_E_ARG, "empty prompt");
+  if (n > c->lay.cap) return fail(c, SVE_E_CAPACITY, "prompt longer than the slot capacity");
+  const int S = c->granted;
+  std::vector<int> res(S);
+  for (int s = 0; s < S; ++s) res[s] = c->resident(s);
+
+  LcpArgs a;
+  memset(&a, 0, sizeof(a));
+  a.out = c->lcp_out();
+  int idxL[SVE_MAX_SLOTS], idxO[SVE_MAX_SLOTS][SVE_MAX_SLOTS];
+  for (int s = 0; s < S; ++s) {
+    idxL[s] = -1;
+    for (int t = 0; t < S; ++t) idxO[s][t] = -1;
+  }
+  for (int s = 0; s < S; ++s) {
+    if (res[s] <= 0) continue;
+    idxL[s] = a.npairs;
+    a.a[a.npairs] = c->tok();
+    a.b[a.npairs] = c->slot_tok(s);
+    a.n[a.npairs++] = std::min(n, res[s]);
+  }
+  for (int s = 0; s < S; ++s)
+    for (int t = s + 1; t < S; ++t) {
+      if (res[s] <= 0 || res[t] <= 0) continue;
+      idxO[s][t] = idxO[t][s] = a.npairs;
+      a.a[a.npairs] = c->slot_tok(s);
+      a.b[a.npairs] = c->slot_tok(t);
+      a.n[a.npairs++] = std::min(res[s], res[t]);
+    }
+  SVE_HIP(c, hipMemcpyAsync(c->tok(), tokens, (size_t)n * 4, hipMemcpyHostToDevice, c->stream));
+  int32_t lcp[kMaxLcpPairs] = {0};
+  if (a.npairs > 0) {
+    SVE_HIP(c, launch_lcp(a, c->stream));
+    SVE_HIP(c, hipMemcpyAsync(lcp, c->lcp_out(), (size_t)a.npairs * 4, hipMemcpyDeviceToHost,
+                              c->stream));
+  }
+  SVE_HIP(c, hipStreamSynchronize(c->stream));
+
+  int Ls[SVE_MAX_SLOTS], Os[SVE_MAX_SLOTS];
+  int n_occ = 0;
+  for (int s = 0; s < S; ++s) n_occ += res[s] > 0;
+  int chosen = -1, r = 0;
+  for (int s = 0; s < S; ++s) {
+    Ls[s] = idxL[s] >= 0 ? lcp[idxL[s]] : 0;
+    Os[s] = 0;
+    for (int t = 0; t < S; ++t)
+      if (t != s && idxO[s][t] >= 0) Os[s] = std::max(Os[s], lcp[idxO[s][t]]);
+  }
+  for (int s = 0; s < S; ++s) {
+    if (res[s] <= 0 || Ls[s] <= 0 || Ls[s] <= Os[s]) continue;
+    const bool lone_ok = c->cfg.match_rule == 1 || Ls[s] == res[s] || n_occ > 1;
+    if (!lone_ok) continue;
+    chosen = s;  // at most one slot can qualify (common-prefix lengths are ultrametric)
+    r = std::min(Ls[s], n - 1);
+    break;
+  }
+  if (chosen < 0) {
+    for (int s = 0; s < S; ++s)
+      if (res[s] <= 0) {
+        chosen = s;
+        r = 0;
+        break;
+      }
+  }
+  if (chosen < 0) {
+    chosen = 0;
+    for (int s = 1; s < S; ++s)
+      if (c->tick[s] < c->tick[chosen]) chosen = s;
+    r = std::min(Ls[chosen], n - 1);
+  }
+  if (!c->cfg.reuse) r = 0;
+
+  SVE_HIP(c, hipMemcpyAsync(c->slot_tok(chosen), c->tok(), (size_t)n * 4,
+                            hipMemcpyDeviceToDevice, c->stream));
+  c->tick[chosen] = ++c->clock;
+  for (int& v : c->kv_len[chosen]) v = r;
+  c->committed[chosen] = n;
+  if (log_on())
+    fprintf(stderr, "[sve] select: n=%d -> slot %d, reused %d (occupied %d)\n", n, chosen, r, n_occ);
+  *slot = chosen;
+  *reused = r;
+  return SVE_OK;
+}
+
+int sve_kv_truncate(sve_ctx* c, int32_t slot, int32_t len) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  if (slot < 0 || slot >= c->granted) return fail(c, SVE_E_SLOT, "slot out of range");
+  if (len < 0 || len > c->resident(slot)) return fail(c, SVE_E_ARG, "truncate can only shorten");
+  for (int& v : c->kv_len[slot]) v = len;
+  return SVE_OK;
+}
+
+int sve_kv_len(const sve_ctx* c, int32_t slot, int32_t layer, int32_t* len) {
+  if (!c || !len) return fail(c, SVE_E_ARG, "null pointer");
+  if (slot < 0 || slot >= c->granted) return fail(c, SVE_E_SLOT, "slot out of range");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, SVE_E_SLOT, "layer out of range");
+  *len = c->kv_len[slot][layer];
+  return SVE_OK;
+}
+
+int sve_extend_attn(sve_ctx* c, int32_t slot, int32_t layer, const void* q, const void* new_k,
+                    const void* new_v, int32_t m, void* out) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  return run_extend(c, 1, &slot, &m, layer, (const uint16_t*)q, (const uint16_t*)new_k,
+                    (const uint16_t*)new_v, (uint16_t*)out);
+}
+
+int sve_extend_attn_batched(sve_ctx* c, int32_t n, const int32_t* slots, const int32_t* ms,
+                            int32_t layer, const void* q, const void* k, const void* v,
+                            void* out) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  if (!slots || !ms) return fail(c, SVE_E_ARG, "null pointer");
+  return run_extend(c, n, slots, ms, layer, (const uint16_t*)q, (const uint16_t*)k,
+                    (const uint16_t*)v, (uint16_t*)out);
+}
+
+int sve_kv_read(sve_ctx* c, int32_t slot, int32_t layer, int32_t start, int32_t len, void* k_out,
+                void* v_out) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  if (slot < 0 || slot >= c->granted) return fail(c, SVE_E_SLOT, "slot out of range");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, SVE_E_SLOT, "layer out of range");
+  if (start < 0 || len < 0 || start + len > c->kv_len[slot][layer])
+    return fail(c, SVE_E_ARG, "rows outside the cached range");
+  if (len > 0 && (!k_out || !v_out)) return fail(c, SVE_E_ARG, "null pointer");
+  SVE_HIP(c, launch_kv_read(c->kbase(slot, layer), c->vtbase(slot, layer), c->cfg.n_kv_heads,
+                            c->cfg.head_dim, c->lay.cap, start, len, (uint16_t*)k_out,
+                            (uint16_t*)v_out, c->stream));
+  return SVE_OK;
+}
+
+size_t sve_w4_packed_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 32 || K % 32) return 0;
+  return w4_packed_bytes(N, K);
+}
+
+int sve_w4_pack(const uint8_t* w, const uint16_t* scales, int32_t N, int32_t K, void* packed,
+                void* hip_stream) {
+  if (N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "need N >= 1 and K % 32 == 0");
+  if (!w || !scales || !packed) return fail(nullptr, SVE_E_ARG, "null pointer");
+  SVE_HIP(nullptr, launch_w4_pack(w, scales, N, K, packed, (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_w4_dequant(const void* packed, int32_t N, int32_t K, float* out, void* hip_stream) {
+  if (N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "need N >= 1 and K % 32 == 0");
+  if (!packed || !out) return fail(nullptr, SVE_E_ARG, "null pointer");
+  SVE_HIP(nullptr, launch_w4_dequant(packed, N, K, out, (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
+                  void* hip_stream) {
+  if (m < 1 || m > 16) return fail(nullptr, SVE_E_ARG, "m must be 1..16");
+  if (N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "need N >= 1 and K % 32 == 0");
+  if (!x || !packed || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
+  SVE_HIP(nullptr, launch_w4_gemv(x, m, packed, N, K, y, (hipStream_t)hip_stream,
+                                  env_int("SVE_GEMV_NT", 0)));
+  return SVE_OK;
+}
+
+int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int32_t* ids,
+                         int32_t topk, const void* packed_all, int32_t E, int32_t N, int32_t K,
+                         float* y, void* hip_stream) {
+  if (m < 1 || m > 16) return fail(nullptr, SVE_E_ARG, "m must be 1..16");
+  if (topk < 1 || topk > 16) return fail(nullptr, SVE_E_ARG, "topk must be 1..16");
+  if (x_per_slot != 0 && x_per_slot != 1) return fail(nullptr, SVE_E_ARG, "x_per_slot is 0 or 1");
+  if (E < 1 || N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "bad E, N or K");
+  if (!x || !ids || !packed_all || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
+  SVE_HIP(nullptr, launch_w4_gemv_routed(x, x_per_slot, m, ids, topk, packed_all, E, N, K, y,
+                                         (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+const char* sve_strerror(int code) {
+  switch (code) {
+    case SVE_OK: return "ok";
+    case SVE_E_ARG: return "invalid argument";
+    case SVE_E_SLOT: return "slot or layer out of range";
+    case SVE_E_CAPACITY: return "capacity exceeded";
+    case SVE_E_HIP: return "HIP runtime error";
+    case SVE_E_STATE: return "call out of order";
+    default: return "unknown status";
+  }
+}
+
+const char* sve_last_error(const sve_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_err.c_str();
+}
+
+}  // extern "C"

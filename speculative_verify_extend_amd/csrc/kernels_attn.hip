@@ -1,0 +1,614 @@
+// Extend-prefill attention on gfx950.
+//
+// m new query rows (positions P .. P+m-1) attend causally to the P cached
+// positions of a resident KV slot plus themselves: row i sees keys 0..P+i.
+// (goinfer, "Turn nine in under half a second", sections "What goinfer does"
+// and "How it works": the cache keeps one key and one value vector per token
+// and layer, and only the tokens after the reused start are prefilled.)
+// Scores are scaled by 1/sqrt(D); q head h reads KV head h / (Hq/Hkv).
+//
+// Store layout per (slot, layer): K [Hkv][cap][D] (row per position) and
+// Vt [Hkv][D][cap] (V transposed, position fastest), bf16. cap is a multiple
+// of 64. Grouped-query rows are packed: for KV head h the packed row index is
+// pr = i*g + j (query row i, query head h*g + j), so one K/V tile serves all g
+// heads of the group.
+//
+// Work is split over key ranges ("splits") aligned to absolute multiples of
+// the split length; each split yields an unnormalised partial (O, running
+// max, sum) merged afterwards in a fixed order.
+#include "common.h"
+#include "launch.h"
+
+namespace sve {
+
+struct SegRef {
+  int s, local;
+};
+
+__device__ __forceinline__ SegRef find_seg(const AttnParams& p, int L) {
+  int s = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxSeg; ++j)
+    if (j < p.nseg && L >= p.seg[j].block_begin) s = j;
+  return SegRef{s, L - p.seg[s].block_begin};
+}
+
+// Linear work index of this workgroup, arranged so that each of the 8 XCDs
+// (workgroups are dealt to XCDs round robin) receives one contiguous range of
+// work: neighbouring row blocks of a KV head then share that XCD's L2.
+__device__ __forceinline__ int xcd_linear(int b, int nb) {
+  const int xcd = b & 7, per = nb >> 3, rem = nb & 7;
+  return xcd * per + min(xcd, rem) + (b >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// KV append: K rows copied, V rows transposed into Vt through LDS.
+// grid (ceil(m/64), Hkv, nseg), block 256.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
+  const AttnSeg& sg = p.seg[blockIdx.z];
+  const int i0 = blockIdx.x * 64;
+  if (i0 >= sg.m) return;
+  const int h = blockIdx.y, Hkv = p.Hkv, cap = p.cap;
+  const int rows = min(64, sg.m - i0);
+  constexpr int CPR = D / 8;
+  uint16_t* K = const_cast<uint16_t*>(sg.K) + (size_t)h * cap * D;
+  uint16_t* Vt = const_cast<uint16_t*>(sg.Vt) + (size_t)h * D * cap;
+  __shared__ uint16_t tile[64][D + 2];
+  for (int c = threadIdx.x; c < rows * CPR; c += 256) {
+    const int r = c / CPR, col = c % CPR;
+    const size_t src = ((size_t)(i0 + r) * Hkv + h) * D + col * 8;
+    store16(K + (size_t)(sg.P + i0 + r) * D + col * 8, load16(sg.nk + src));
+    const u32x4 v = load16(sg.nv + src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r][col * 8 + 2 * e] = (uint16_t)(v[e] & 0xFFFFu);
+      tile[r][col * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D * 64; c += 256) {
+    const int d = c >> 6, r = c & 63;
+    if (r < rows) Vt[(size_t)d * cap + sg.P + i0 + r] = tile[r][d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path. Workgroup = 4 waves; each wave owns RT tiles of 16 packed rows,
+// so a workgroup covers 64*RT packed rows of one KV head and one key split.
+// Per 64-key tile, K [64][D] and Vt [D][64] are staged once in LDS (double
+// buffered through registers) and shared by the four waves.
+//   S^T = K Q^T   (A = 16 keys x 32 d from LDS, B = Q^T held in registers)
+//   O^T += Vt P^T (A = 16 d x 32 keys from LDS, B = P^T straight from the
+//                  S^T accumulators, rounded to bf16)
+// Within a 32-key chunk the 16-key MFMA sub-tiles take keys
+// 8*(j/4) + 4*sub + j%4, so that lane (row, kb) ends up holding keys
+// 8*kb .. 8*kb+7 of the chunk: exactly its B operand for the PV product, and
+// its Vt A operand is then one 16-byte LDS read. Each lane owns one packed
+// row (lane % 16): the online-softmax row statistics need only two cross-lane
+// steps (lanes l, l^16, l^32, l^48 hold the same row).
+// ---------------------------------------------------------------------------
+template <int D, int RT>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
+  constexpr int DC = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int KS = D + 8;   // LDS row stride of the K tile (bf16)
+  constexpr int VS = 64 + 8;  // LDS row stride of the Vt tile (bf16)
+  constexpr int KCH = (64 * D / 8) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VS];
+
+  const int L = xcd_linear(blockIdx.x, gridDim.x);
+  const SegRef ref = find_seg(prm, L);
+  const AttnSeg& sg = prm.seg[ref.s];
+  const int split = ref.local % sg.splits;
+  const int rest = ref.local / sg.splits;
+  const int rb = rest % sg.row_blocks;
+  const int kvh = rest / sg.row_blocks;
+  const int g = prm.g, Hq = prm.Hq, cap = prm.cap;
+  const int P = sg.P, m = sg.m, R = m * g;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kb = lane >> 4, col = lane & 15;
+
+  const int wg_row0 = rb * 64 * RT;
+  const int wg_last = min(R - 1, wg_row0 + 64 * RT - 1);
+  const int kstart = split * sg.split_keys;
+  const int kend = min(P + wg_last / g + 1, kstart + sg.split_keys);
+  if (kstart >= kend) return;  // no row of this block sees this split
+
+  int lim[RT], qi[RT], qh[RT];
+  bool rvalid[RT];
+  bf16x8 qreg[RT][DC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int pr = wg_row0 + wave * 16 * RT + 16 * rt + col;
+    rvalid[rt] = pr < R;
+    const int i = rvalid[rt] ? pr / g : 0;
+    qi[rt] = i;
+    qh[rt] = kvh * g + (rvalid[rt] ? pr % g : 0);
+    lim[rt] = rvalid[rt] ? P + i : 0;
+    const uint16_t* qrow = sg.q + ((size_t)i * Hq + qh[rt]) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rvalid[rt]) v = load16(qrow + 32 * dc + 8 * kb);
+      qreg[rt][dc] = as_bf16x8(v);
+    }
+  }
+
+  f32x4 O[RT][DT];
+  float mrun[RT], lrun[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    mrun[rt] = -INFINITY;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint16_t* Kg = sg.K + (size_t)kvh * cap * D;
+  const uint16_t* Vg = sg.Vt + (size_t)kvh * D * cap;
+  const int kv_end = P + m;
+  const float cs = prm.c;
+
+  u32x4 kst[KCH], vst[KCH];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int row = c / (D / 8), cc = c % (D / 8);
+      kst[u] = load16(Kg + (size_t)(kt + row) * D + cc * 8);
+      const int d = c >> 3, kc = c & 7;
+      u32x4 v = load16(Vg + (size_t)d * cap + kt + kc * 8);
+      const int key0 = kt + kc * 8;
+      if (key0 + 8 > kv_end) {  // positions past the sequence: zero V
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t w = v[e];
+          if (key0 + 2 * e >= kv_end) w &= 0xFFFF0000u;
+          if (key0 + 2 * e + 1 >= kv_end) w &= 0x0000FFFFu;
+          v[e] = w;
+        }
+      }
+      vst[u] = v;
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int row = c / (D / 8), cc = c % (D / 8);
+      store16(&Ks[buf][row * KS + cc * 8], kst[u]);
+      const int d = c >> 3, kc = c & 7;
+      store16(&Vs[buf][d * VS + kc * 8], vst[u]);
+    }
+  };
+
+  gload(kstart);
+  swrite(0);
+  __syncthreads();
+  int buf = 0;
+  for (int kt = kstart; kt < kend; kt += 64) {
+    const bool more = kt + 64 < kend;
+    if (more) gload(kt + 64);
+
+    f32x4 S[RT][2][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) S[rt][c][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kappa = 32 * c + 8 * (col >> 2) + 4 * sub + (col & 3);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const bf16x8 kop = as_bf16x8(load16(&Ks[buf][kappa * KS + 32 * dc + 8 * kb]));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            S[rt][c][sub] = mfma16x16x32(kop, qreg[rt][dc], S[rt][c][sub]);
+        }
+      }
+    }
+
+    bf16x8 pb[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt + 32 * c + 8 * kb + 4 * sub + i;
+            const float v = (key <= lim[rt]) ? S[rt][c][sub][i] : -INFINITY;
+            S[rt][c][sub][i] = v;
+            mx = fmaxf(mx, v);
+          }
+      mx = fmaxf(mx, xor_shfl(mx, 16));
+      mx = fmaxf(mx, xor_shfl(mx, 32));
+      const float mnew = fmaxf(mrun[rt], mx * cs);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2f(mrun[rt] - muse);
+      mrun[rt] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 pk;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = exp2f(fmaf(S[rt][c][sub][i], cs, -muse));
+            const float p1 = exp2f(fmaf(S[rt][c][sub][i + 1], cs, -muse));
+            const uint32_t w = pack_bf16x2(p0, p1);
+            pk[2 * sub + (i >> 1)] = w;
+            psum += bf16_to_f32(w & 0xFFFFu) + bf16_to_f32(w >> 16);
+          }
+        pb[rt][c] = as_bf16x8(pk);
+      }
+      lrun[rt] = lrun[rt] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[rt][dt][i] *= alpha;
+    }
+
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 vop =
+            as_bf16x8(load16(&Vs[buf][(16 * dt + col) * VS + 32 * c + 8 * kb]));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) O[rt][dt] = mfma16x16x32(vop, pb[rt][c], O[rt][dt]);
+      }
+    }
+
+    if (more) swrite(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = lrun[rt];
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    if (!rvalid[rt]) continue;
+    const size_t orow = ((size_t)qi[rt] * Hq + qh[rt]) * D;
+    if (sg.splits == 1) {
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x2 w;
+        w[0] = pack_bf16x2(O[rt][dt][0] * inv, O[rt][dt][1] * inv);
+        w[1] = pack_bf16x2(O[rt][dt][2] * inv, O[rt][dt][3] * inv);
+        *reinterpret_cast<u32x2*>(sg.out + orow + 16 * dt + 4 * kb) = w;
+      }
+    } else {
+      const size_t wrow = ((size_t)split * m * Hq) * D + orow;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(sg.ws_o + wrow + 16 * dt + 4 * kb) = O[rt][dt];
+      if (kb == 0) {
+        float* ml = sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 2;
+        ml[0] = mrun[rt];
+        ml[1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU path for short suffixes. Workgroup = (KV head, block of 16 packed rows,
+// key split); its 4 waves take the 64-key tiles of the split in turn. For the
+// scores a lane owns one key (dot products by v_dot2_f32_bf16 against q pairs
+// broadcast from LDS); for the value product a lane owns D/64 columns of Vt
+// (dot2 of bf16 probability pairs against key-adjacent V pairs). The four
+// waves' partial states are merged in LDS in a fixed order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, xor_shfl(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += xor_shfl(v, o);
+  return v;
+}
+
+constexpr int kValuRows = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
+  constexpr int DP = D / 2;   // bf16 pairs per row
+  constexpr int DPL = D / 64; // Vt columns per lane
+  __shared__ uint32_t qs[kValuRows][DP];                 // q rows, bf16 pairs
+  __shared__ uint32_t ps[4][kValuRows][32];              // per wave: p pairs
+  __shared__ float wm[4][kValuRows], wl[4][kValuRows];
+  __shared__ float wo[4][kValuRows][D];
+
+  const int L = xcd_linear(blockIdx.x, gridDim.x);
+  const SegRef ref = find_seg(prm, L);
+  const AttnSeg& sg = prm.seg[ref.s];
+  const int split = ref.local % sg.splits;
+  const int rest = ref.local / sg.splits;
+  const int rb = rest % sg.row_blocks;
+  const int kvh = rest / sg.row_blocks;
+  const int g = prm.g, Hq = prm.Hq, cap = prm.cap;
+  const int P = sg.P, m = sg.m, R = m * g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  const int row0 = rb * kValuRows;
+  const int nrows = min(kValuRows, R - row0);
+  const int wg_last = row0 + nrows - 1;
+  const int kstart = split * sg.split_keys;
+  const int kend = min(P + wg_last / g + 1, kstart + sg.split_keys);
+  if (kstart >= kend) return;
+
+  for (int c = threadIdx.x; c < kValuRows * DP; c += 256) {
+    const int r = c / DP, dp = c % DP;
+    uint32_t v = 0;
+    if (r < nrows) {
+      const int pr = row0 + r;
+      const int i = pr / g, h = kvh * g + pr % g;
+      v = reinterpret_cast<const uint32_t*>(sg.q + ((size_t)i * Hq + h) * D)[dp];
+    }
+    qs[r][dp] = v;
+  }
+  __syncthreads();
+
+  float mrun[kValuRows], lrun[kValuRows];
+  float oacc[kValuRows][DPL];
+#pragma unroll
+  for (int r = 0; r < kValuRows; ++r) {
+    mrun[r] = -INFINITY;
+    lrun[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) oacc[r][j] = 0.f;
+  }
+
+  const uint16_t* Kg = sg.K + (size_t)kvh * cap * D;
+  const uint16_t* Vg = sg.Vt + (size_t)kvh * D * cap;
+  const int kv_end = P + m;
+  const float cs = prm.c;
+
+  for (int kt = kstart + 64 * wave; kt < kend; kt += 256) {
+    // scores: lane = key kt + lane
+    const int key = kt + lane;
+    uint32_t kr[DP];
+    const uint16_t* krow = Kg + (size_t)key * D;  // key < cap always (kt + 64 <= cap)
+#pragma unroll
+    for (int c = 0; c < DP / 4; ++c) {
+      const u32x4 v = load16(krow + 8 * c);
+      kr[4 * c + 0] = v[0];
+      kr[4 * c + 1] = v[1];
+      kr[4 * c + 2] = v[2];
+      kr[4 * c + 3] = v[3];
+    }
+    uint32_t vr[DPL][32];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const uint16_t* vrow = Vg + (size_t)(lane + 64 * j) * cap + kt;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4 v = load16(vrow + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = kt + 8 * c + 2 * e;
+          uint32_t w = v[e];
+          if (k0 >= kv_end) w &= 0xFFFF0000u;
+          if (k0 + 1 >= kv_end) w &= 0x0000FFFFu;
+          vr[j][4 * c + e] = w;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kValuRows; ++r) {
+      if (r < nrows) {
+        float s = 0.f;
+#pragma unroll
+        for (int dp = 0; dp < DP; ++dp) s = dot2_bf16(kr[dp], qs[r][dp], s);
+        const int pr = row0 + r;
+        const int limr = P + pr / g;
+        s = (key <= limr) ? s : -INFINITY;
+        const float mx = wave_max(s);
+        const float mnew = fmaxf(mrun[r], mx * cs);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2f(mrun[r] - muse);
+        mrun[r] = mnew;
+        const float p = exp2f(fmaf(s, cs, -muse));
+        const uint32_t pw = pack_bf16x2(p, 0.f) & 0xFFFFu;
+        lrun[r] = lrun[r] * alpha + bf16_to_f32(pw);
+        // key-adjacent pairs of p: lane 2t holds the low half, 2t+1 the high
+        const uint32_t nb = (uint32_t)__shfl_xor((int)pw, 1, 64);
+        if ((lane & 1) == 0) ps[wave][r][lane >> 1] = pw | (nb << 16);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) oacc[r][j] *= alpha;
+      }
+    }
+    // make this wave's p visible to all its lanes (wave-local LDS traffic)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < kValuRows; ++r) {
+      if (r < nrows) {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) {
+          float o = oacc[r][j];
+#pragma unroll
+          for (int t = 0; t < 32; ++t) o = dot2_bf16(vr[j][t], ps[wave][r][t], o);
+          oacc[r][j] = o;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // merge the four waves
+#pragma unroll
+  for (int r = 0; r < kValuRows; ++r) {
+    const float l = wave_sum(lrun[r]);
+    if (lane == 0) {
+      wm[wave][r] = mrun[r];
+      wl[wave][r] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) wo[wave][r][lane + 64 * j] = oacc[r][j];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < nrows * D; c += 256) {
+    const int r = c / D, d = c % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][r]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = exp2f(wm[w][r] - Mu);
+      o += sc * wo[w][r][d];
+      l += sc * wl[w][r];
+    }
+    const int pr = row0 + r;
+    const int i = pr / g, h = kvh * g + pr % g;
+    if (sg.splits == 1) {
+      reinterpret_cast<__bf16*>(sg.out)[((size_t)i * Hq + h) * D + d] = (__bf16)(o / l);
+    } else {
+      sg.ws_o[(((size_t)split * m + i) * Hq + h) * D + d] = o;
+      if (d == 0) {
+        float* ml = sg.ws_ml + (((size_t)split * m + i) * Hq + h) * 2;
+        ml[0] = M;
+        ml[1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split combine: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// splits that contain at least one key the row can see, in split order.
+// grid over rows (i, h) of all pieces; 4 columns per thread.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+  constexpr int TPR = D / 4;  // threads per (i, h) row
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / TPR;
+  const int c4 = (int)(t % TPR) * 4;
+  if (row >= (long long)p.total_rows * p.Hq) return;
+  const int grow = (int)(row / p.Hq), h = (int)(row % p.Hq);
+  int s = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxSeg; ++j)
+    if (j < p.nseg && grow >= p.seg[j].row_begin) s = j;
+  const AttnSeg& sg = p.seg[s];
+  if (sg.splits == 1) return;
+  const int i = grow - sg.row_begin;
+  const int nvalid = min(sg.splits, (sg.P + i) / sg.split_keys + 1);
+  float M = -INFINITY;
+  for (int sp = 0; sp < nvalid; ++sp)
+    M = fmaxf(M, sg.ws_ml[(((size_t)sp * sg.m + i) * p.Hq + h) * 2]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int sp = 0; sp < nvalid; ++sp) {
+    const float* ml = sg.ws_ml + (((size_t)sp * sg.m + i) * p.Hq + h) * 2;
+    const float sc = exp2f(ml[0] - M);
+    l += sc * ml[1];
+    const f32x4 v =
+        *reinterpret_cast<const f32x4*>(sg.ws_o + (((size_t)sp * sg.m + i) * p.Hq + h) * D + c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += sc * v[e];
+  }
+  const float inv = 1.f / l;
+  u32x2 w;
+  w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+  w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(sg.out + ((size_t)i * p.Hq + h) * D + c4) = w;
+}
+
+// KV read-back (test export): K rows and transposed-back V rows.
+__global__ __launch_bounds__(256) void kv_read_kernel(const uint16_t* K, const uint16_t* Vt,
+                                                      int Hkv, int D, int cap, int start, int len,
+                                                      uint16_t* k_out, uint16_t* v_out) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)len * Hkv * D) return;
+  const int d = (int)(t % D);
+  const int h = (int)((t / D) % Hkv);
+  const int i = (int)(t / ((long long)D * Hkv));
+  k_out[t] = K[((size_t)h * cap + start + i) * D + d];
+  v_out[t] = Vt[((size_t)h * D + d) * cap + start + i];
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+int attn_rows_per_block(int path) { return path == kPathValu ? kValuRows : 64 * 2; }
+
+hipError_t launch_kv_append(const AttnParams& p, hipStream_t st) {
+  int maxm = 0;
+  for (int s = 0; s < p.nseg; ++s) maxm = p.seg[s].m > maxm ? p.seg[s].m : maxm;
+  if (maxm == 0) return hipSuccess;
+  const dim3 grid((maxm + 63) / 64, p.Hkv, p.nseg);
+  if (p.D == 128)
+    hipLaunchKernelGGL(kv_append_kernel<128>, grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<64>, grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnParams& p, int path, hipStream_t st) {
+  if (p.total_blocks == 0) return hipSuccess;
+  const dim3 grid(p.total_blocks), block(256);
+  if (path == kPathValu) {
+    if (p.D == 128)
+      hipLaunchKernelGGL(attn_valu_kernel<128>, grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL(attn_valu_kernel<64>, grid, block, 0, st, p);
+  } else {
+    if (p.D == 128)
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnParams& p, hipStream_t st) {
+  bool any = false;
+  for (int s = 0; s < p.nseg; ++s) any |= p.seg[s].splits > 1 && p.seg[s].m > 0;
+  if (!any) return hipSuccess;
+  const long long threads = (long long)p.total_rows * p.Hq * (p.D / 4);
+  const int blocks = (int)((threads + 255) / 256);
+  if (p.D == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(blocks), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_read(const uint16_t* K, const uint16_t* Vt, int Hkv, int D, int cap,
+                          int start, int len, uint16_t* k_out, uint16_t* v_out, hipStream_t st) {
+  const long long total = (long long)len * Hkv * D;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_read_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, K,
+                     Vt, Hkv, D, cap, start, len, k_out, v_out);
+  return hipGetLastError();
+}
+
+}  // namespace sve

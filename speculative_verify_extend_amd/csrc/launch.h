@@ -1,0 +1,72 @@
+// Host-side launchers of the gfx950 kernels (internal to libsve).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sve {
+
+// ---- int4 weights -----------------------------------------------------------
+size_t w4_packed_bytes(int N, int K);
+hipError_t launch_w4_pack(const uint8_t* w, const uint16_t* s, int N, int K, void* packed,
+                          hipStream_t st);
+hipError_t launch_w4_dequant(const void* packed, int N, int K, float* out, hipStream_t st);
+hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K, float* y,
+                          hipStream_t st, int nt_override);
+hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int32_t* ids,
+                                 int topk, const void* packed_all, int E, int N, int K, float* y,
+                                 hipStream_t st);
+
+// ---- attention ------------------------------------------------------------------
+constexpr int kMaxSeg = 4;
+
+// One (slot, layer) piece of an extend call. The KV store of a slot and layer
+// is K [Hkv][cap][D] followed by Vt [Hkv][D][cap] (bf16).
+struct AttnSeg {
+  const uint16_t* K;
+  const uint16_t* Vt;
+  const uint16_t* q;   // [m][Hq][D]
+  const uint16_t* nk;  // new rows [m][Hkv][D]
+  const uint16_t* nv;
+  uint16_t* out;       // [m][Hq][D]
+  float* ws_o;         // [splits][m][Hq][D]
+  float* ws_ml;        // [splits][m][Hq][2]
+  int P, m;
+  int row_blocks;      // per KV head
+  int splits, split_keys;
+  int block_begin;     // first linear workgroup of this piece
+  int row_begin;       // first output row of this piece in a combined launch
+};
+
+struct AttnParams {
+  AttnSeg seg[kMaxSeg];
+  int nseg;
+  int Hq, Hkv, g, D, cap;
+  int total_blocks;
+  int total_rows;      // sum of m over pieces
+  float c;             // log2(e) / sqrt(D)
+};
+
+enum AttnPath { kPathValu = 0, kPathMfma = 1 };
+
+// rows of packed (query row, head-in-group) per workgroup for each path
+int attn_rows_per_block(int path);
+hipError_t launch_kv_append(const AttnParams& p, hipStream_t st);
+hipError_t launch_attn(const AttnParams& p, int path, hipStream_t st);
+hipError_t launch_attn_combine(const AttnParams& p, hipStream_t st);
+// copy rows [start, start+len) of one slot/layer back to [len][Hkv][D] (test export)
+hipError_t launch_kv_read(const uint16_t* K, const uint16_t* Vt, int Hkv, int D, int cap,
+                          int start, int len, uint16_t* k_out, uint16_t* v_out, hipStream_t st);
+
+// ---- slot matcher ----------------------------------------------------------------
+constexpr int kMaxLcpPairs = 16;
+struct LcpArgs {
+  const int32_t* a[kMaxLcpPairs];
+  const int32_t* b[kMaxLcpPairs];
+  int n[kMaxLcpPairs];
+  int npairs;
+  int32_t* out;
+};
+hipError_t launch_lcp(const LcpArgs& args, hipStream_t st);
+
+}  // namespace sve

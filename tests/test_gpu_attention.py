@@ -1,0 +1,225 @@
+"""GPU parity of extend-prefill attention against the oracle (max-abs 1e-2,
+bf16 in/out, fp32 accumulation), on both kernel paths, with and without key
+splits, plus the invariants the pages fix: extend over a cached prefix equals
+the tail of a full prefill, token-by-token equals one pass, and the cached
+K/V rows are exactly the appended ones."""
+import numpy as np
+import pytest
+import torch
+
+import speculative_verify_extend_amd as sve
+import synth
+from oracle.attention import extend_attention
+from tests.gpu_helpers import (announce, dev_bf16, env, host_bits, host_f64_of_bf16,
+                               require_gpu)
+
+pytestmark = pytest.mark.gpu
+ATTN_TOL = 1e-2  # max-abs against the fp64 oracle
+
+PATHS = {"valu": dict(SVE_MFMA_MIN_ROWS=100000), "mfma": dict(SVE_MFMA_MIN_ROWS=1)}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _store(hq, hkv, d, cap, max_rows, n_slots=1, n_layers=1):
+    return sve.KVSlots(n_slots, n_layers, hq, hkv, d, cap, max_rows)
+
+
+def _run_case(hq, hkv, d, prefix, m, path, seed=0, split=0, prefill_path=None):
+    """Fill a slot with `prefix` rows, then extend by m rows; returns
+    (gpu output of the m rows, oracle output, case dict)."""
+    c = synth.attention_case(seed, hq, hkv, d, prefix, m)
+    st = _store(hq, hkv, d, prefix + m + 64, max(prefix, m, 1))
+    toks = np.arange(prefix + m, dtype=np.int32)
+    slot, reused = st.kv_slot_select(toks)
+    assert (slot, reused) == (0, 0)
+    if prefix:
+        with env(**PATHS[prefill_path or path]):
+            st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]),
+                           dev_bf16(c["v_prefix"]))
+    with env(SVE_KV_SPLIT=split, **PATHS[path]):
+        out = st.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"]))
+    k_all = np.concatenate([c["k_prefix"], c["k"]])
+    v_all = np.concatenate([c["v_prefix"], c["v"]])
+    want = extend_attention(c["q"], k_all, v_all, prefix)
+    return host_f64_of_bf16(out), want, c, st
+
+
+CASES = [
+    # hq, hkv, d, prefix, m
+    (4, 2, 64, 64, 8),      # tiny single layer: 64 cached + 8 new rows
+    (4, 2, 64, 0, 64),      # tiny prefix fill (full prefill)
+    (4, 2, 64, 0, 1),       # one row, one key
+    (8, 8, 128, 100, 13),   # no GQA, ragged prefix
+    (28, 4, 128, 200, 37),  # 7B-like heads, ragged rows
+    (32, 8, 128, 130, 5),   # 9B-like heads, verify-sized suffix
+    (4, 1, 128, 300, 70),   # wide group, several row blocks
+]
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "h%d-%d-d%d-P%d-m%d" % c)
+def test_extend_matches_oracle(case, path):
+    hq, hkv, d, prefix, m = case
+    announce(f"extend {case} path={path}")
+    got, want, _, _ = _run_case(hq, hkv, d, prefix, m, path)
+    assert np.abs(got - want).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("split", [1, 2, 5, 16])
+def test_key_splits(path, split):
+    announce(f"splits={split} path={path}")
+    got, want, _, _ = _run_case(8, 2, 128, 700, 21, path, seed=3, split=split)
+    assert np.abs(got - want).max() <= ATTN_TOL
+
+
+def test_turn9_full_size():
+    """Agent-turn replay turn 9: 1668 cached + 254 new rows, 28 q / 4 KV heads,
+    D 128, default launch configuration (the one the bench times)."""
+    announce("turn9 full")
+    got, want, _, _ = _run_case(28, 4, 128, 1668, 254, "mfma", seed=2)
+    assert np.abs(got - want).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_verify_full_size(m):
+    """Speculative verify: 2048 cached + m rows, 32 q / 8 KV heads, D 128, on
+    the default path for that m."""
+    announce(f"verify full m={m}")
+    c = synth.attention_case(3, 32, 8, 128, 2048, m)
+    st = _store(32, 8, 128, 2048 + 8, 2048)
+    st.kv_slot_select(np.arange(2048 + m, dtype=np.int32))
+    st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]), dev_bf16(c["v_prefix"]))
+    out = st.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"]))
+    want = extend_attention(c["q"], np.concatenate([c["k_prefix"], c["k"]]),
+                            np.concatenate([c["v_prefix"], c["v"]]), 2048)
+    assert np.abs(host_f64_of_bf16(out) - want).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_extend_equals_tail_of_full_prefill(path):
+    """Extend over a cached prefix == the last rows of a from-scratch prefill
+    of the whole sequence, both on the GPU."""
+    hq, hkv, d, P, m = 8, 2, 128, 150, 30
+    announce(f"tail-of-prefill path={path}")
+    got, _, c, _ = _run_case(hq, hkv, d, P, m, path, seed=5)
+    st = _store(hq, hkv, d, P + m + 64, P + m)
+    st.kv_slot_select(np.arange(P + m, dtype=np.int32))
+    with env(**PATHS[path]):
+        full = st.extend_attn(0, 0, dev_bf16(np.concatenate([c["q_prefix"], c["q"]])),
+                              dev_bf16(np.concatenate([c["k_prefix"], c["k"]])),
+                              dev_bf16(np.concatenate([c["v_prefix"], c["v"]])))
+    assert np.abs(host_f64_of_bf16(full)[P:] - got).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_token_by_token_equals_one_pass_bitwise(path):
+    """Within one kernel path and without key splits, m one-row calls give the
+    same bits as one m-row call: each row's arithmetic depends only on its own
+    query and the keys it sees, in absolute-position tile order."""
+    hq, hkv, d, P, m = 8, 2, 128, 90, 12
+    c = synth.attention_case(7, hq, hkv, d, P, m)
+    announce(f"token-by-token path={path}")
+    outs = []
+    for mode in ("one", "many"):
+        st = _store(hq, hkv, d, P + m + 64, P + m)
+        st.kv_slot_select(np.arange(P + m, dtype=np.int32))
+        with env(SVE_KV_SPLIT=1, **PATHS[path]):
+            st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]),
+                           dev_bf16(c["v_prefix"]))
+            if mode == "one":
+                outs.append(host_bits(st.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]),
+                                                     dev_bf16(c["v"]))))
+            else:
+                rows = [host_bits(st.extend_attn(0, 0, dev_bf16(c["q"][i:i + 1]),
+                                                 dev_bf16(c["k"][i:i + 1]),
+                                                 dev_bf16(c["v"][i:i + 1]))) for i in range(m)]
+                outs.append(np.concatenate(rows))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_paths_agree_within_tolerance():
+    """The VALU and MFMA paths differ only by rounding (bf16 probabilities in
+    the MFMA value product); both stay within the oracle tolerance."""
+    announce("paths agree")
+    a, want, _, _ = _run_case(16, 4, 128, 400, 9, "valu", seed=8)
+    b, _, _, _ = _run_case(16, 4, 128, 400, 9, "mfma", seed=8)
+    assert np.abs(a - b).max() <= 2 * ATTN_TOL
+    assert np.abs(a - want).max() <= ATTN_TOL and np.abs(b - want).max() <= ATTN_TOL
+
+
+def test_cached_rows_are_the_appended_rows():
+    hq, hkv, d, P, m = 4, 2, 64, 70, 9
+    announce("kv read")
+    _, _, c, st = _run_case(hq, hkv, d, P, m, "mfma", seed=9)
+    k, v = st.kv_read(0, 0, 0, P + m)
+    assert np.array_equal(host_bits(k), np.concatenate([c["k_prefix"], c["k"]]))
+    assert np.array_equal(host_bits(v), np.concatenate([c["v_prefix"], c["v"]]))
+
+
+def test_deterministic_repeats():
+    hq, hkv, d, P, m = 28, 4, 128, 500, 60
+    c = synth.attention_case(10, hq, hkv, d, P, m)
+    st = _store(hq, hkv, d, P + m + 64, P + m)
+    st.kv_slot_select(np.arange(P + m, dtype=np.int32))
+    st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]), dev_bf16(c["v_prefix"]))
+    q, k, v = dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"])
+    announce("determinism")
+    first = st.extend_attn(0, 0, q, k, v)
+    for _ in range(30):
+        st.kv_truncate(0, P)
+        assert torch.equal(st.extend_attn(0, 0, q, k, v), first)
+
+
+def test_zero_rows_is_noop_and_state_errors():
+    st = _store(4, 2, 64, 128, 64)
+    z = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    zk = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    st.kv_slot_select(np.arange(10, dtype=np.int32))
+    st.extend_attn(0, 0, z, zk, zk)
+    assert st.kv_len(0) == 0
+    q = torch.zeros((11, 4, 64), dtype=torch.bfloat16, device="cuda")
+    kk = torch.zeros((11, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sve.SveError) as e:
+        st.extend_attn(0, 0, q, kk, kk)  # 11 rows > the 10 selected tokens
+    assert e.value.code == -5
+    with pytest.raises(sve.SveError) as e:
+        st.extend_attn(1, 0, q[:1], kk[:1], kk[:1])
+    assert e.value.code == -2
+
+
+def test_batched_matches_single_slot_calls():
+    """Four slots in one launch (4B-like heads, ~30-row questions on
+    ~800-token states) equal four separate calls and the oracle."""
+    hq, hkv, d = 32, 8, 128
+    Ps, ms = [800, 830, 861, 905], [30, 24, 36, 27]
+    st_b = sve.KVSlots(4, 1, hq, hkv, d, 1024, 1024)
+    st_s = sve.KVSlots(4, 1, hq, hkv, d, 1024, 1024)
+    cases = [synth.attention_case(40 + i, hq, hkv, d, Ps[i], ms[i]) for i in range(4)]
+    announce("batched")
+    for st in (st_b, st_s):
+        for i in range(4):
+            toks = np.concatenate([[i + 1], np.arange(Ps[i] + ms[i] - 1)]).astype(np.int32)
+            slot, r = st.kv_slot_select(toks)
+            assert (slot, r) == (i, 0)
+            st.extend_attn(slot, 0, dev_bf16(cases[i]["q_prefix"]),
+                           dev_bf16(cases[i]["k_prefix"]), dev_bf16(cases[i]["v_prefix"]))
+    q = dev_bf16(np.concatenate([c["q"] for c in cases]))
+    k = dev_bf16(np.concatenate([c["k"] for c in cases]))
+    v = dev_bf16(np.concatenate([c["v"] for c in cases]))
+    out_b = host_f64_of_bf16(st_b.extend_attn_batched([0, 1, 2, 3], ms, 0, q, k, v))
+    row = 0
+    for i in range(4):
+        c = cases[i]
+        single = host_f64_of_bf16(st_s.extend_attn(i, 0, dev_bf16(c["q"]), dev_bf16(c["k"]),
+                                                   dev_bf16(c["v"])))
+        want = extend_attention(c["q"], np.concatenate([c["k_prefix"], c["k"]]),
+                                np.concatenate([c["v_prefix"], c["v"]]), Ps[i])
+        part = out_b[row:row + ms[i]]
+        assert np.abs(part - want).max() <= ATTN_TOL
+        assert np.abs(part - single).max() <= ATTN_TOL
+        row += ms[i]
