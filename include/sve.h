@@ -55,7 +55,8 @@ typedef struct {
   int32_t n_kv_heads; /* Hkv */
   int32_t head_dim;   /* D: 64 or 128 */
   int32_t capacity;   /* max tokens per slot (rounded up to a multiple of 64) */
-  int32_t max_rows;   /* max new rows per extend call (sum over a batched call) */
+  int32_t max_rows;   /* max new rows per extend call (sum over a batched call),
+                         1..4*capacity; sizes the split workspace */
   int32_t reuse;      /* 0: select always reports 0 reused tokens */
   int32_t match_rule; /* 0: lone-slot clause on (default); 1: literal rule */
 } sve_config;
@@ -91,7 +92,9 @@ int sve_set_stream(sve_ctx* ctx, void* hip_stream);
  *     (r <= n-1, so the last prompt token always runs through the model).
  * Commits: the slot's prompt becomes `tokens`, every layer's cached length
  * becomes r, the slot becomes most recently used. Only tokens whose K/V rows
- * are cached in every layer take part in matching. A slot is eligible when
+ * are cached in every layer take part in matching; a slot stays claimed (not
+ * empty) from its first select on, even before its rows are prefilled, so
+ * several prompts may be placed before one batched extend. A slot is eligible when
  * its common start with the prompt is > 0, exceeds its common start with
  * every other occupied slot, and either covers the whole slot or some other
  * slot is occupied (match_rule 1 drops this last clause).
@@ -184,6 +187,18 @@ int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32
 int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int32_t* expert_ids,
                          int32_t topk, const void* packed_all, int32_t E, int32_t N, int32_t K,
                          float* y, void* hip_stream);
+
+/* ---- measurement probes (not part of the computation) ---------------------
+ * Plain streaming read and plain copy of device memory, used to measure the
+ * achievable HBM bandwidth beside the published peak and to calibrate the
+ * hardware traffic counters against a kernel that moves a known byte count.
+ *   src, dst: device buffers of `bytes` bytes (a multiple of 16).
+ *   blocks: workgroups of 256 threads (1..65536); unroll: loads in flight per
+ *   thread (1, 2, 4 or 8); sink: device uint32 [blocks*256], written.
+ * Errors: SVE_E_ARG, SVE_E_HIP. */
+int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll, void* sink,
+                   void* hip_stream);
+int sve_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* hip_stream);
 
 /* Message for a status code. */
 const char* sve_strerror(int code);

@@ -28,6 +28,9 @@ the model (section "What we got wrong", the one-token-short bug).
 
 Only tokens whose K/V rows are resident in every layer take part in matching:
 T_s is the committed prompt of slot s cut to min over layers of kv_len[s].
+A slot counts as empty only while no prompt has been selected into it: one
+handed to a conversation stays claimed while its prefill is still pending, so
+several prompts can be placed before any of them is prefilled.
 """
 from __future__ import annotations
 
@@ -103,7 +106,7 @@ class SlotOracle:
             s = el[0]
             r = min(lcp(prompt, self.resident(s)), n - 1)
         else:
-            empty = [t for t in range(self.n_slots) if not self.occupied(t)]
+            empty = [t for t in range(self.n_slots) if self.committed[t] == 0]
             if empty:
                 s, r = empty[0], 0
             else:

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import SveError, check
 
 __all__ = ["KVSlots", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m",
-           "w4_gemv_m_routed", "SveError", "load_library"]
+           "w4_gemv_m_routed", "probe_read", "probe_copy", "SveError", "load_library"]
 
 
 def load_library():
@@ -203,3 +203,21 @@ def w4_gemv_m_routed(x: torch.Tensor, expert_ids: torch.Tensor, packed_all: torc
     check(lib.sve_w4_gemv_m_routed(_ptr(x), int(bool(x_per_slot)), m, _ptr(expert_ids), topk,
                                    _ptr(packed_all), n_experts, n, k, _ptr(y), _stream()))
     return y
+
+
+def probe_read(src: torch.Tensor, blocks: int, unroll: int = 4) -> torch.Tensor:
+    """Streaming read of a device buffer (measurement probe)."""
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=src.device)
+    check(_lib.load().sve_probe_read(_ptr(src), src.numel() * src.element_size(), blocks, unroll,
+                                     _ptr(sink), _stream()))
+    return sink
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, blocks: int) -> None:
+    """Plain device copy (measurement probe and counter calibration)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst differ in size")
+    check(_lib.load().sve_probe_copy(_ptr(src), _ptr(dst), n, blocks, _stream()))

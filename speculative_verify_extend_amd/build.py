@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsve.so")
 ARCH = os.environ.get("SVE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "kernels_w4.hip", "kernels_attn.hip", "kernels_slot.hip"]
+SOURCES = ["api.cpp", "kernels_w4.hip", "kernels_attn.hip", "kernels_slot.hip",
+           "kernels_probe.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -55,7 +56,7 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
 def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="sve_build_") as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
-        with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
             futs = [ex.submit(_compile, s, o, verbose) for s, o in zip(SOURCES, objs)]
             for f in futs:
                 f.result()

@@ -42,8 +42,8 @@ bool config_ok(const sve_config* c, std::string* why) {
     return *why = "n_q_heads must be a positive multiple of n_kv_heads", false;
   if (c->head_dim != 64 && c->head_dim != 128) return *why = "head_dim must be 64 or 128", false;
   if (c->capacity < 1 || c->capacity > (1 << 20)) return *why = "capacity out of range", false;
-  if (c->max_rows < 1 || c->max_rows > c->capacity)
-    return *why = "max_rows must be 1..capacity", false;
+  if (c->max_rows < 1 || c->max_rows > SVE_MAX_SLOTS * c->capacity)
+    return *why = "max_rows must be 1..4*capacity", false;
   if (c->match_rule != 0 && c->match_rule != 1) return *why = "match_rule must be 0 or 1", false;
   return true;
 }
@@ -148,7 +148,8 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
     const int keys = sg.P + sg.m;
-    int S = forced > 0 ? forced : (target + base - 1) / std::max(base, 1);
+    // as many splits as keep the grid within one round of workgroups
+    int S = forced > 0 ? forced : target / std::max(base, 1);
     S = std::max(1, std::min(S, kMaxSplits));
     S = std::min(S, (keys + 63) / 64);
     int sk = (keys + S - 1) / S;
@@ -354,9 +355,9 @@ int sve_kv_slot_select(sve_ctx* c, const int32_t* tokens, int32_t n, int32_t* sl
     r = std::min(Ls[s], n - 1);
     break;
   }
-  if (chosen < 0) {
+  if (chosen < 0) {  // a slot is empty until a prompt has been selected into it
     for (int s = 0; s < S; ++s)
-      if (res[s] <= 0) {
+      if (c->committed[s] == 0) {
         chosen = s;
         r = 0;
         break;
@@ -454,7 +455,7 @@ int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32
   if (N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "need N >= 1 and K % 32 == 0");
   if (!x || !packed || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
   SVE_HIP(nullptr, launch_w4_gemv(x, m, packed, N, K, y, (hipStream_t)hip_stream,
-                                  env_int("SVE_GEMV_NT", 0)));
+                                  env_int("SVE_GEMV_WGS_PER_CU", 0)));
   return SVE_OK;
 }
 
@@ -468,6 +469,23 @@ int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int
   if (!x || !ids || !packed_all || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
   SVE_HIP(nullptr, launch_w4_gemv_routed(x, x_per_slot, m, ids, topk, packed_all, E, N, K, y,
                                          (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll, void* sink,
+                   void* hip_stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16) return fail(nullptr, SVE_E_ARG, "bad probe buffer");
+  if (blocks < 1 || blocks > 65536) return fail(nullptr, SVE_E_ARG, "blocks must be 1..65536");
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
+    return fail(nullptr, SVE_E_ARG, "unroll must be 1, 2, 4 or 8");
+  SVE_HIP(nullptr, launch_probe_read(src, bytes, blocks, unroll, sink, (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* hip_stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16) return fail(nullptr, SVE_E_ARG, "bad probe buffer");
+  if (blocks < 1 || blocks > 65536) return fail(nullptr, SVE_E_ARG, "blocks must be 1..65536");
+  SVE_HIP(nullptr, launch_probe_copy(src, dst, bytes, blocks, (hipStream_t)hip_stream));
   return SVE_OK;
 }
 

@@ -21,6 +21,12 @@
 
 namespace sve {
 
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 struct SegRef {
   int s, local;
 };
@@ -43,19 +49,21 @@ __device__ __forceinline__ int xcd_linear(int b, int nb) {
 
 // ---------------------------------------------------------------------------
 // KV append: K rows copied, V rows transposed into Vt through LDS.
-// grid (ceil(m/64), Hkv, nseg), block 256.
+// grid (ceil(m/16), Hkv, nseg), block 256: 16 new rows of one KV head.
 // ---------------------------------------------------------------------------
+constexpr int kAppendRows = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
   const AttnSeg& sg = p.seg[blockIdx.z];
-  const int i0 = blockIdx.x * 64;
+  const int i0 = blockIdx.x * kAppendRows;
   if (i0 >= sg.m) return;
   const int h = blockIdx.y, Hkv = p.Hkv, cap = p.cap;
-  const int rows = min(64, sg.m - i0);
+  const int rows = min(kAppendRows, sg.m - i0);
   constexpr int CPR = D / 8;
   uint16_t* K = const_cast<uint16_t*>(sg.K) + (size_t)h * cap * D;
   uint16_t* Vt = const_cast<uint16_t*>(sg.Vt) + (size_t)h * D * cap;
-  __shared__ uint16_t tile[64][D + 2];
+  __shared__ uint16_t tile[D][kAppendRows + 2];
   for (int c = threadIdx.x; c < rows * CPR; c += 256) {
     const int r = c / CPR, col = c % CPR;
     const size_t src = ((size_t)(i0 + r) * Hkv + h) * D + col * 8;
@@ -63,14 +71,14 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
     const u32x4 v = load16(sg.nv + src);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tile[r][col * 8 + 2 * e] = (uint16_t)(v[e] & 0xFFFFu);
-      tile[r][col * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+      tile[col * 8 + 2 * e][r] = (uint16_t)(v[e] & 0xFFFFu);
+      tile[col * 8 + 2 * e + 1][r] = (uint16_t)(v[e] >> 16);
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < D * 64; c += 256) {
-    const int d = c >> 6, r = c & 63;
-    if (r < rows) Vt[(size_t)d * cap + sg.P + i0 + r] = tile[r][d];
+  for (int c = threadIdx.x; c < D * kAppendRows; c += 256) {
+    const int d = c / kAppendRows, r = c % kAppendRows;
+    if (r < rows) Vt[(size_t)d * cap + sg.P + i0 + r] = tile[d][r];
   }
 }
 
@@ -117,6 +125,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
   const int kstart = split * sg.split_keys;
   const int kend = min(P + wg_last / g + 1, kstart + sg.split_keys);
   if (kstart >= kend) return;  // no row of this block sees this split
+  const int wg_min_lim = P + wg_row0 / g;
 
   int lim[RT], qi[RT], qh[RT];
   bool rvalid[RT];
@@ -129,20 +138,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
     qi[rt] = i;
     qh[rt] = kvh * g + (rvalid[rt] ? pr % g : 0);
     lim[rt] = rvalid[rt] ? P + i : 0;
+    // padded rows read a live query row; their outputs are never stored
     const uint16_t* qrow = sg.q + ((size_t)i * Hq + qh[rt]) * D;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (rvalid[rt]) v = load16(qrow + 32 * dc + 8 * kb);
-      qreg[rt][dc] = as_bf16x8(v);
-    }
+    for (int dc = 0; dc < DC; ++dc) qreg[rt][dc] = as_bf16x8(load16(qrow + 32 * dc + 8 * kb));
   }
 
   f32x4 O[RT][DT];
-  float mrun[RT], lrun[RT];
+  float mref[RT], lrun[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    mrun[rt] = -INFINITY;
+    mref[rt] = -INFINITY;
     lrun[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -161,33 +167,36 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
       const int row = c / (D / 8), cc = c % (D / 8);
       kst[u] = load16(Kg + (size_t)(kt + row) * D + cc * 8);
       const int d = c >> 3, kc = c & 7;
-      u32x4 v = load16(Vg + (size_t)d * cap + kt + kc * 8);
-      const int key0 = kt + kc * 8;
-      if (key0 + 8 > kv_end) {  // positions past the sequence: zero V
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t w = v[e];
-          if (key0 + 2 * e >= kv_end) w &= 0xFFFF0000u;
-          if (key0 + 2 * e + 1 >= kv_end) w &= 0x0000FFFFu;
-          v[e] = w;
-        }
-      }
-      vst[u] = v;
+      vst[u] = load16(Vg + (size_t)d * cap + kt + kc * 8);
     }
   };
-  auto swrite = [&](int buf) {
+  // Loaded values are only touched here, a full tile of compute after the
+  // loads were issued: V at positions past the sequence is zeroed so stale
+  // cache contents can never reach the value product.
+  auto swrite = [&](int buf, int kt) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int c = threadIdx.x + 256 * u;
       const int row = c / (D / 8), cc = c % (D / 8);
       store16(&Ks[buf][row * KS + cc * 8], kst[u]);
       const int d = c >> 3, kc = c & 7;
-      store16(&Vs[buf][d * VS + kc * 8], vst[u]);
+      u32x4 v = vst[u];
+      const int key0 = kt + kc * 8;
+      if (key0 + 8 > kv_end) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t w = v[e];
+          w = (key0 + 2 * e >= kv_end) ? (w & 0xFFFF0000u) : w;
+          w = (key0 + 2 * e + 1 >= kv_end) ? (w & 0x0000FFFFu) : w;
+          v[e] = w;
+        }
+      }
+      store16(&Vs[buf][d * VS + kc * 8], v);
     }
   };
 
   gload(kstart);
-  swrite(0);
+  swrite(0, kstart);
   __syncthreads();
   int buf = 0;
   for (int kt = kstart; kt < kend; kt += 64) {
@@ -216,7 +225,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
       }
     }
 
+    // Keys past a row's causal limit only occur in tiles that reach beyond
+    // the smallest limit of the workgroup's rows.
+    const bool edge = kt + 63 > wg_min_lim;
     bf16x8 pb[RT][2];
+    bool grow = false;
+    float mcand[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float mx = -INFINITY;
@@ -226,18 +240,39 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = kt + 32 * c + 8 * kb + 4 * sub + i;
-            const float v = (key <= lim[rt]) ? S[rt][c][sub][i] : -INFINITY;
-            S[rt][c][sub][i] = v;
+            float v = S[rt][c][sub][i];
+            if (edge) {
+              const int key = kt + 32 * c + 8 * kb + 4 * sub + i;
+              v = (key <= lim[rt]) ? v : -INFINITY;
+              S[rt][c][sub][i] = v;
+            }
             mx = fmaxf(mx, v);
           }
       mx = fmaxf(mx, xor_shfl(mx, 16));
       mx = fmaxf(mx, xor_shfl(mx, 32));
-      const float mnew = fmaxf(mrun[rt], mx * cs);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(mrun[rt] - muse);
-      mrun[rt] = mnew;
-      float psum = 0.f;
+      mcand[rt] = mx * cs;
+      // the reference max moves only when a row's max grows by more than 8
+      // (log2 units): probabilities then stay below 2^8 and the running
+      // output is rescaled rarely
+      grow |= mcand[rt] > mref[rt] + 8.f;
+    }
+    if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float mnew = fmaxf(mref[rt], mcand[rt]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mref[rt] - mnew);
+        mref[rt] = mnew;
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[rt][dt][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float muse = (mref[rt] == -INFINITY) ? 0.f : mref[rt];
+      float psum = lrun[rt];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         u32x4 pk;
@@ -249,15 +284,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
             const float p1 = exp2f(fmaf(S[rt][c][sub][i + 1], cs, -muse));
             const uint32_t w = pack_bf16x2(p0, p1);
             pk[2 * sub + (i >> 1)] = w;
-            psum += bf16_to_f32(w & 0xFFFFu) + bf16_to_f32(w >> 16);
+            psum = dot2_bf16(w, 0x3F803F80u, psum);  // + both bf16 values exactly
           }
         pb[rt][c] = as_bf16x8(pk);
       }
-      lrun[rt] = lrun[rt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[rt][dt][i] *= alpha;
+      lrun[rt] = psum;
     }
 
 #pragma unroll
@@ -271,7 +302,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
       }
     }
 
-    if (more) swrite(buf ^ 1);
+    if (more) swrite(buf ^ 1, kt + 64);
     __syncthreads();
     buf ^= 1;
   }
@@ -299,7 +330,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
         *reinterpret_cast<f32x4*>(sg.ws_o + wrow + 16 * dt + 4 * kb) = O[rt][dt];
       if (kb == 0) {
         float* ml = sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 2;
-        ml[0] = mrun[rt];
+        ml[0] = mref[rt];
         ml[1] = l;
       }
     }
@@ -314,12 +345,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
 // (dot2 of bf16 probability pairs against key-adjacent V pairs). The four
 // waves' partial states are merged in LDS in a fixed order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, xor_shfl(v, o));
@@ -564,7 +589,7 @@ hipError_t launch_kv_append(const AttnParams& p, hipStream_t st) {
   int maxm = 0;
   for (int s = 0; s < p.nseg; ++s) maxm = p.seg[s].m > maxm ? p.seg[s].m : maxm;
   if (maxm == 0) return hipSuccess;
-  const dim3 grid((maxm + 63) / 64, p.Hkv, p.nseg);
+  const dim3 grid((maxm + kAppendRows - 1) / kAppendRows, p.Hkv, p.nseg);
   if (p.D == 128)
     hipLaunchKernelGGL(kv_append_kernel<128>, grid, dim3(256), 0, st, p);
   else

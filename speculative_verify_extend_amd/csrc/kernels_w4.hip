@@ -21,6 +21,8 @@
 // One wave-wide 16-byte load of a nibble block is 1 KB contiguous and gives
 // every lane exactly the B operand of four v_mfma_f32_16x16x32_bf16 (one per
 // group). Rows past N and groups past K/32 are padded with code 8 and scale 0.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -104,120 +106,123 @@ __global__ __launch_bounds__(256) void w4_dequant_kernel(const uint8_t* __restri
 // ---------------------------------------------------------------------------
 // m-row GEMV core.
 //
-// The workgroup owns NT row tiles (16 output rows each) and all of K; its 4
-// waves take contiguous quarters of the k quads. Per group the weights enter
-// v_mfma_f32_16x16x32_bf16 as B = bf16(128 + code) (one v_and_or per element
-// pair), the activations as A (row r of the MFMA tile = input row r, zero
-// beyond the live rows), and the accumulator starts at C0 = -136 * sum(x) of
-// the group (one extra MFMA per group against a constant -136 operand, shared
-// by all row tiles), so D = sum x * (code - 8). D is then scaled by the
-// group's fp16 scale into the fp32 accumulators. The 16-row MFMA is used as a
-// multiply engine only: the kernel stays a single pass over the weight stream
-// and costs the same for every m <= 16.
+// Workgroup = 8 waves. The k quads are cut into KS contiguous slices and the
+// waves are laid out as (8/KS tile lanes) x (KS slices); a workgroup owns
+// NT*(8/KS) row tiles of 16 output rows. Each wave streams its slice of its
+// tiles through a ring of PD quads in flight (weights, scales and the
+// activation operands together), so the loads of quad q+PD are issued as
+// soon as quad q is consumed and the weight stream never drains.
+//
+// Per group the weights enter v_mfma_f32_16x16x32_bf16 as B = bf16(128 +
+// code) (one v_and_or per element pair), the activations as A (row r of the
+// MFMA tile = input row r, zero beyond the live rows), and the accumulator
+// starts at C0 = -136 * sum(x) of the group (one extra MFMA per group against
+// a constant -136 operand, shared by the NT tiles), so D = sum x * (code - 8).
+// D is then scaled by the group's fp16 scale into fp32 accumulators. The
+// 16-row MFMA is only the multiply engine: the kernel is a single pass over
+// the weight stream and costs the same for every m <= 16. Partial sums of
+// the KS slices are added in LDS in a fixed order.
 // ---------------------------------------------------------------------------
 
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 8;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-// quads of weight loads issued together per wave: 8 KB of the weight stream
-// in flight per wave whatever the number of row tiles
-template <int NT>
-struct GemvBatch {
-  static constexpr int value = 8 / NT;
-};
+constexpr int kGemvPD = 4;  // quads in flight per wave
 
 template <int NT>
 struct GemvAcc {
   f32x4 v[NT];
 };
 
-// xrow: this lane's activation row (A row lane%16), or nullptr for a padded
-// row. Weight tiles t0 .. t0+nt-1 (nt <= NT), quads [q0, q1).
 template <int NT>
-__device__ __forceinline__ void gemv_core(const uint16_t* __restrict__ xrow, int K,
+struct GemvSlot {
+  u32x4 w[NT];
+  u32x2 s[NT];
+  u32x4 x[4];
+};
+
+// xrow: this lane's activation row (A row lane%16; padded rows pass a live
+// row, whose MFMA output rows are never stored). Tiles t0 .. t0+nt-1
+// (1 <= nt <= NT), quads [q0, q1). Every load is issued unconditionally from
+// a valid address (tiles, quads and k clamped into range): a load under a
+// divergent branch whose other side writes the same registers forces a full
+// drain of the memory pipeline, which would serialise the stream. Groups past
+// K carry zero scales, so whatever activations they meet contribute nothing.
+template <int NT>
+__device__ __forceinline__ void gemv_core(const uint16_t* __restrict__ xrow, bool xlive, int K,
                                           const uint8_t* __restrict__ nib,
                                           const uint8_t* __restrict__ scl, int Q, int t0, int nt,
                                           int q0, int q1, GemvAcc<NT>& acc) {
-  constexpr int kGemvBatch = GemvBatch<NT>::value;
   const int lane = threadIdx.x & 63;
   const int kb = lane >> 4;
   u32x4 m136;
   m136[0] = m136[1] = m136[2] = m136[3] = 0xC308C308u;  // bf16(-136) x 8
   const bf16x8 neg136 = as_bf16x8(m136);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  if (q0 >= q1) return;
 
-  auto load_x = [&](int q, u32x4 (&xa)[4]) {
+  auto issue = [&](int q, GemvSlot<NT>& sl) {
+    q = min(q, q1 - 1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t blk = (size_t)(t0 + min(t, nt - 1)) * Q + q;
+      sl.w[t] = load16(nib + blk * 1024 + lane * 16);
+      sl.s[t] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + (lane & 15) * 8);
+    }
+    if (xlive) {  // lanes of padded rows keep zeros (no write on the other side)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = min(128 * q + 32 * j + 8 * kb, K - 8);
+        sl.x[j] = load16(xrow + k);
+      }
+    }
+  };
+  auto consume = [&](const GemvSlot<NT>& sl) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = 128 * q + 32 * j + 8 * kb;
-      if (xrow != nullptr && k < K) {
-        xa[j] = load16(xrow + k);
-      } else {
-        xa[j][0] = xa[j][1] = xa[j][2] = xa[j][3] = 0u;
+      const bf16x8 a = as_bf16x8(sl.x[j]);
+      const f32x4 c0 = mfma16x16x32(a, neg136, zero4);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t dw = sl.w[t][j];
+        u32x4 b;
+        b[0] = (dw & 0x000F000Fu) | 0x43004300u;
+        b[1] = ((dw >> 4) & 0x000F000Fu) | 0x43004300u;
+        b[2] = ((dw >> 8) & 0x000F000Fu) | 0x43004300u;
+        b[3] = ((dw >> 12) & 0x000F000Fu) | 0x43004300u;
+        const f32x4 d = mfma16x16x32(a, as_bf16x8(b), c0);
+        const uint32_t sw = sl.s[t][j >> 1];
+        const float sc = f16_bits_to_f32((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc.v[t][i] = fmaf(sc, d[i], acc.v[t][i]);
       }
     }
   };
 
-  u32x4 xnext[4];
-  if (q0 < q1) load_x(q0, xnext);
-  for (int qb = q0; qb < q1; qb += kGemvBatch) {
-    const int nq = min(kGemvBatch, q1 - qb);
-    u32x4 wv[kGemvBatch][NT];
-    u32x2 sv[kGemvBatch][NT];
+  GemvSlot<NT> ring[kGemvPD];
 #pragma unroll
-    for (int p = 0; p < kGemvBatch; ++p) {
-      if (p < nq) {
+  for (int p = 0; p < kGemvPD; ++p)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t < nt) {
-            const size_t blk = (size_t)(t0 + t) * Q + (qb + p);
-            wv[p][t] = load16(nib + blk * 1024 + lane * 16);
-            sv[p][t] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + (lane & 15) * 8);
-          }
-        }
-      }
-    }
+    for (int j = 0; j < 4; ++j) ring[p].x[j] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int p = 0; p < kGemvBatch; ++p) {
-      if (p < nq) {
-        u32x4 xa[4];
+  for (int p = 0; p < kGemvPD; ++p)
+    if (q0 + p < q1) issue(q0 + p, ring[p]);  // wave-uniform
+  for (int qb = q0; qb < q1; qb += kGemvPD) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xa[j] = xnext[j];
-        if (qb + p + 1 < q1) load_x(qb + p + 1, xnext);
-        bf16x8 a[4];
-        f32x4 c0[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[j] = as_bf16x8(xa[j]);
-          c0[j] = mfma16x16x32(a[j], neg136, zero4);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t < nt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t dw = wv[p][t][j];
-              u32x4 b;
-              b[0] = (dw & 0x000F000Fu) | 0x43004300u;
-              b[1] = ((dw >> 4) & 0x000F000Fu) | 0x43004300u;
-              b[2] = ((dw >> 8) & 0x000F000Fu) | 0x43004300u;
-              b[3] = ((dw >> 12) & 0x000F000Fu) | 0x43004300u;
-              const f32x4 d = mfma16x16x32(a[j], as_bf16x8(b), c0[j]);
-              const uint32_t sw = sv[p][t][j >> 1];
-              const float s = f16_bits_to_f32((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc.v[t][i] = fmaf(s, d[i], acc.v[t][i]);
-            }
-          }
-        }
+    for (int p = 0; p < kGemvPD; ++p) {
+      const int q = qb + p;
+      if (q < q1) {
+        consume(ring[p]);
+        if (q + kGemvPD < q1) issue(q + kGemvPD, ring[p]);  // wave-uniform
       }
     }
   }
 }
 
-// Sum the four waves' accumulators in a fixed order and hand each output
-// (tile t, MFMA row r, column c) to store(t, r, c, value).
+// Sum the KS slices' accumulators in a fixed order and hand each output
+// (tile, MFMA row r, column c) to store(tile, r, c, value). Tiles are
+// numbered ts*NT + t for tile lane ts.
 template <int NT, class Store>
-__device__ __forceinline__ void gemv_reduce(GemvAcc<NT>& acc, int nt, Store store) {
+__device__ __forceinline__ void gemv_reduce(GemvAcc<NT>& acc, int KS, int tiles, Store store) {
   __shared__ float red[kGemvWaves][NT][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -225,39 +230,227 @@ __device__ __forceinline__ void gemv_reduce(GemvAcc<NT>& acc, int nt, Store stor
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][t][i][lane] = acc.v[t][i];
   __syncthreads();
-  // thread -> (i, lane) pair; each thread handles every tile
-  const int i = threadIdx.x >> 6;  // 0..3
-  const int l = threadIdx.x & 63;
-  for (int t = 0; t < nt; ++t) {
-    float s = red[0][t][i][l];
-#pragma unroll
-    for (int w = 1; w < kGemvWaves; ++w) s += red[w][t][i][l];
-    store(t, 4 * (l >> 4) + i, l & 15, s);
+  const int TPW = kGemvWaves / KS;
+  for (int idx = threadIdx.x; idx < TPW * NT * 256; idx += kGemvThreads) {
+    const int l = idx & 63, i = (idx >> 6) & 3, tt = idx >> 8;
+    const int ts = tt / NT, t = tt % NT;
+    if (tt >= tiles) continue;
+    float sum = red[ts * KS][t][i][l];
+    for (int k = 1; k < KS; ++k) sum += red[ts * KS + k][t][i][l];
+    store(tt, 4 * (l >> 4) + i, l & 15, sum);
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint16_t* __restrict__ x,
-                                                               int m,
-                                                               const uint8_t* __restrict__ nib,
-                                                               const uint8_t* __restrict__ scl,
-                                                               int N, int K, int Q, int n_tiles,
-                                                               float* __restrict__ y) {
-  const int t0 = blockIdx.x * NT;
-  const int nt = min(NT, n_tiles - t0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15;
-  const uint16_t* xrow = (r < m) ? x + (size_t)r * K : nullptr;
-  const int per = (Q + kGemvWaves - 1) / kGemvWaves;
-  const int q0 = min(Q, wave * per), q1 = min(Q, q0 + per);
-  GemvAcc<NT> acc;
+// Choose the k-slice count: 8 slices when there are at least 8 quads, fewer
+// (and more tile lanes per workgroup) for short K.
+__host__ __device__ inline int gemv_ks(int Q) { return Q >= 8 ? 8 : Q >= 4 ? 4 : Q >= 2 ? 2 : 1; }
+
+// Dense m-row GEMV. Two straight-line pipelines (no data-dependent branches
+// around loads, so the compiler's wait counts stay exact and loads overlap):
+//
+//  * short K (at most four quads per wave slice): a grid of about one
+//    workgroup per CU walks a contiguous run of tile groups (TPW = 8/KS row
+//    tiles each). Each wave loads the activation operands of its k slice
+//    once (live rows only) and double-buffers the weight/scale blocks of
+//    tile groups: the blocks of group g+2 are requested while group g is
+//    consumed.
+//  * long K: one tile group per workgroup; each wave walks its slice in
+//    chunks of four quads (weights, scales and activations), double
+//    buffered.
+// Steps past the end of a run or slice re-read a valid block and are
+// neutralised by a zero scale. After each tile group the KS partial sums are
+// added in LDS in a fixed order and stored.
+
+template <int QPW>
+struct ShortBuf {
+  u32x4 w[QPW];
+  u32x2 s[QPW];
+};
+
+__device__ __forceinline__ void mfma_group(const bf16x8 a, uint32_t dw, float sc, bf16x8 neg136,
+                                           f32x4& acc) {
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 c0 = mfma16x16x32(a, neg136, zero4);
+  u32x4 b;
+  b[0] = (dw & 0x000F000Fu) | 0x43004300u;
+  b[1] = ((dw >> 4) & 0x000F000Fu) | 0x43004300u;
+  b[2] = ((dw >> 8) & 0x000F000Fu) | 0x43004300u;
+  b[3] = ((dw >> 12) & 0x000F000Fu) | 0x43004300u;
+  const f32x4 d = mfma16x16x32(a, as_bf16x8(b), c0);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc.v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemv_core<NT>(xrow, K, nib, scl, Q, t0, nt, q0, q1, acc);
-  gemv_reduce<NT>(acc, nt, [&](int t, int row, int col, float v) {
-    const int n = 16 * (t0 + t) + col;
-    if (row < m && n < N) y[(size_t)row * N + n] = v;
-  });
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, d[i], acc[i]);
+}
+
+__device__ __forceinline__ float scale_of(u32x2 sv, int j) {
+  const uint32_t sw = sv[j >> 1];
+  return f16_bits_to_f32((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+}
+
+// Add the KS slices of one tile group in LDS and store the outputs.
+__device__ __forceinline__ void gemv_group_store(float (*red)[4][64], f32x4& acc, int KS, int TPW,
+                                                 int tile0, bool live, int n_tiles, int m, int N,
+                                                 float* __restrict__ y) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  if (live) {
+    for (int id = threadIdx.x; id < TPW * 256; id += kGemvThreads) {
+      const int l = id & 63, i = (id >> 6) & 3, tsi = id >> 8;
+      const int tile = tile0 + tsi;
+      float sum = red[tsi * KS][i][l];
+      for (int k2 = 1; k2 < KS; ++k2) sum += red[tsi * KS + k2][i][l];
+      const int row = 4 * (l >> 4) + i, n = 16 * tile + (l & 15);
+      if (tile < n_tiles && row < m && n < N) y[(size_t)row * N + n] = sum;
+    }
+  }
+  __syncthreads();
+}
+
+template <int QPW>
+__global__ __launch_bounds__(kGemvThreads) void w4_gemv_short_kernel(
+    const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
+    const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
+  __shared__ float red[kGemvWaves][4][64];
+  const int KS = gemv_ks(Q), TPW = kGemvWaves / KS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ts = wave / KS, ksl = wave % KS, kb = lane >> 4, r = lane & 15;
+  const int n_groups = (n_tiles + TPW - 1) / TPW;
+  const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
+  const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
+  if (g0 >= g1) return;
+  const int q0 = ksl * QPW;           // first quad of this wave's slice
+  const int nq = max(0, min(QPW, Q - q0));  // real quads in the slice
+  const bool xlive = r < m;
+  const uint16_t* xrow = x + (size_t)(xlive ? r : 0) * K;
+  u32x4 m136;
+  m136[0] = m136[1] = m136[2] = m136[3] = 0xC308C308u;
+  const bf16x8 neg136 = as_bf16x8(m136);
+
+  u32x4 xr[QPW][4];
+#pragma unroll
+  for (int a = 0; a < QPW; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xr[a][j] = u32x4{0u, 0u, 0u, 0u};
+      if (xlive && a < nq) xr[a][j] = load16(xrow + min(128 * (q0 + a) + 32 * j + 8 * kb, K - 8));
+    }
+
+  auto issue = [&](int g, ShortBuf<QPW>& b) {
+    const int tile = min(min(g, g1 - 1) * TPW + ts, n_tiles - 1);
+#pragma unroll
+    for (int a = 0; a < QPW; ++a) {
+      const size_t blk = (size_t)tile * Q + min(q0 + a, Q - 1);
+      b.w[a] = load16(nib + blk * 1024 + lane * 16);
+      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + r * 8);
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](const ShortBuf<QPW>& b) {
+#pragma unroll
+    for (int a = 0; a < QPW; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = (a < nq) ? scale_of(b.s[a], j) : 0.f;
+        mfma_group(as_bf16x8(xr[a][j]), b.w[a][j], sc, neg136, acc);
+      }
+  };
+
+  // The scheduling fences keep each buffer's loads contiguous in issue order
+  // on every path into the loop, so the wait before consuming a buffer only
+  // covers that buffer.
+  ShortBuf<QPW> A, B;
+  issue(g0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(g0 + 1, B);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int g = g0; g < g1; g += 2) {
+    consume(A);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(g + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    gemv_group_store(red, acc, KS, TPW, g * TPW, true, n_tiles, m, N, y);
+    consume(B);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(g + 3, B);
+    __builtin_amdgcn_sched_barrier(0);
+    gemv_group_store(red, acc, KS, TPW, (g + 1) * TPW, g + 1 < g1, n_tiles, m, N, y);
+  }
+}
+
+constexpr int kLongChunk = 2;  // quads per chunk
+
+struct LongBuf {
+  u32x4 w[kLongChunk];
+  u32x2 s[kLongChunk];
+  u32x4 x[kLongChunk][4];
+};
+
+__global__ __launch_bounds__(kGemvThreads) void w4_gemv_long_kernel(
+    const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
+    const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
+  __shared__ float red[kGemvWaves][4][64];
+  const int KS = gemv_ks(Q), TPW = kGemvWaves / KS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ts = wave / KS, ksl = wave % KS, kb = lane >> 4, r = lane & 15;
+  const int g = blockIdx.x;
+  const int tile = min(g * TPW + ts, n_tiles - 1);
+  const int per = (Q + KS - 1) / KS;
+  const int q0 = ksl * per;
+  const int nq = max(0, min(per, Q - q0));
+  const int nchunks = (per + kLongChunk - 1) / kLongChunk;  // same for every wave
+  const bool xlive = r < m;
+  const uint16_t* xrow = x + (size_t)(xlive ? r : 0) * K;
+  u32x4 m136;
+  m136[0] = m136[1] = m136[2] = m136[3] = 0xC308C308u;
+  const bf16x8 neg136 = as_bf16x8(m136);
+
+  LongBuf A, B;
+#pragma unroll
+  for (int a = 0; a < kLongChunk; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) A.x[a][j] = B.x[a][j] = u32x4{0u, 0u, 0u, 0u};
+  auto issue = [&](int c, LongBuf& b) {
+#pragma unroll
+    for (int a = 0; a < kLongChunk; ++a) {
+      const int q = min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1);
+      const size_t blk = (size_t)tile * Q + q;
+      b.w[a] = load16(nib + blk * 1024 + lane * 16);
+      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + r * 8);
+      if (xlive) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b.x[a][j] = load16(xrow + min(128 * q + 32 * j + 8 * kb, K - 8));
+      }
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](int c, const LongBuf& b) {
+#pragma unroll
+    for (int a = 0; a < kLongChunk; ++a) {
+      const bool real = c * kLongChunk + a < nq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = real ? scale_of(b.s[a], j) : 0.f;
+        mfma_group(as_bf16x8(b.x[a][j]), b.w[a][j], sc, neg136, acc);
+      }
+    }
+  };
+  issue(0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1, B);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = 0; c < nchunks; c += 2) {
+    consume(c, A);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(c + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c + 3, B);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  gemv_group_store(red, acc, KS, TPW, g * TPW, true, n_tiles, m, N, y);
 }
 
 // Expert-routed form. Block (pair slot ps, tile group): the expert of pair ps
@@ -274,11 +467,15 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_routed_kernel(
   const int e = ids[ps];
   for (int p = 0; p < ps; ++p)
     if (ids[p] == e) return;  // an earlier pair slot owns this expert
-  const int t0 = blockIdx.x * NT;
-  const int nt = min(NT, n_tiles - t0);
+  const int KS = gemv_ks(Q), TPW = kGemvWaves / KS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int per = (Q + kGemvWaves - 1) / kGemvWaves;
-  const int q0 = min(Q, wave * per), q1 = min(Q, q0 + per);
+  const int ts = wave / KS, ks = wave % KS;
+  const int wg_t0 = blockIdx.x * TPW * NT;
+  const int wg_tiles = min(TPW * NT, n_tiles - wg_t0);
+  const int t0 = wg_t0 + ts * NT;
+  const int nt = max(0, min(NT, n_tiles - t0));
+  const int per = (Q + KS - 1) / KS;
+  const int q0 = min(Q, ks * per), q1 = min(Q, q0 + per);
   const bool valid = (e >= 0 && e < E);
   const uint8_t* nib = packed_all + (valid ? (size_t)e * expert_bytes : 0);
   const uint8_t* scl = nib + scale_off;
@@ -286,50 +483,47 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_routed_kernel(
   __shared__ int rows[16];
   int start = ps;  // pairs with this expert all sit at or after ps
   while (true) {
-    // gather up to 16 pairs routed to e, starting at `start`
     __syncthreads();
     if (threadIdx.x == 0) {
-      int c = 0, p = start;
-      for (; p < npairs && c < 16; ++p)
+      int c = 0;
+      for (int p = start; p < npairs && c < 16; ++p)
         if (ids[p] == e) rows[c++] = p;
       for (int j = c; j < 16; ++j) rows[j] = -1;
     }
     __syncthreads();
     int next = npairs;
     {
-      // first pair after the gathered ones (uniform)
       int last = -1;
       for (int j = 0; j < 16; ++j)
         if (rows[j] >= 0) last = rows[j];
       if (last >= 0)
         for (int p = last + 1; p < npairs; ++p)
-          if (ids[p] == e) { next = p; break; }
+          if (ids[p] == e) {
+            next = p;
+            break;
+          }
     }
     if (!valid) {
       // out-of-range expert id: its outputs are NaN
       for (int j = 0; j < 16; ++j) {
         const int p = rows[j];
         if (p < 0) continue;
-        for (int c = threadIdx.x; c < nt * 16; c += kGemvThreads) {
-          const int n = 16 * t0 + c;
+        for (int c = threadIdx.x; c < wg_tiles * 16; c += kGemvThreads) {
+          const int n = 16 * wg_t0 + c;
           if (n < N) y[(size_t)p * N + n] = __builtin_nanf("");
         }
       }
     } else {
-      const int mr = lane & 15;
-      const int pr = rows[mr];
-      const uint16_t* xrow = nullptr;
-      if (pr >= 0) {
-        const int r = pr / topk;
-        xrow = x_per_slot ? x + (size_t)pr * K : x + (size_t)r * K;
-      }
+      const int pr = max(rows[lane & 15], rows[0]);
+      const bool xlive = rows[lane & 15] >= 0;
+      const uint16_t* xrow = x_per_slot ? x + (size_t)pr * K : x + (size_t)(pr / topk) * K;
       GemvAcc<NT> acc;
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc.v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gemv_core<NT>(xrow, K, nib, scl, Q, t0, nt, q0, q1, acc);
-      gemv_reduce<NT>(acc, nt, [&](int t, int row, int col, float v) {
+      if (nt > 0) gemv_core<NT>(xrow, xlive, K, nib, scl, Q, t0, nt, q0, q1, acc);
+      gemv_reduce<NT>(acc, KS, wg_tiles, [&](int tt, int row, int col, float v) {
         const int p = rows[row];
-        const int n = 16 * (t0 + t) + col;
+        const int n = 16 * (wg_t0 + tt) + col;
         if (p >= 0 && n < N) y[(size_t)p * N + n] = v;
       });
     }
@@ -366,36 +560,36 @@ hipError_t launch_w4_dequant(const void* packed, int N, int K, float* out, hipSt
   return hipGetLastError();
 }
 
-// Row tiles per workgroup: enough workgroups to cover the 256 CUs at least
-// twice before a workgroup takes more than one tile.
-static int gemv_nt(int n_tiles, int groups) {
-  const long long per_cu = 512;
-  if ((long long)n_tiles * groups >= per_cu * 4) return 4;
-  if ((long long)n_tiles * groups >= per_cu * 2) return 2;
-  return 1;
-}
-
 hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K, float* y,
-                          hipStream_t st, int nt_override) {
+                          hipStream_t st, int wgs_per_cu) {
   const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
   const uint8_t* nib = (const uint8_t*)packed;
   const uint8_t* scl = nib + (size_t)n_tiles * Q * 1024;
-  const int nt = nt_override > 0 ? nt_override : gemv_nt(n_tiles, 1);
-  const dim3 block(kGemvThreads);
+  const int KS = gemv_ks(Q), tpw = kGemvWaves / KS;
+  const int n_groups = (n_tiles + tpw - 1) / tpw;
+  const int per = (Q + KS - 1) / KS;
   const uint16_t* xp = (const uint16_t*)x;
-  switch (nt) {
-    case 4:
-      hipLaunchKernelGGL(w4_gemv_kernel<4>, dim3((n_tiles + 3) / 4), block, 0, st, xp, m, nib, scl,
-                         N, K, Q, n_tiles, y);
-      break;
-    case 2:
-      hipLaunchKernelGGL(w4_gemv_kernel<2>, dim3((n_tiles + 1) / 2), block, 0, st, xp, m, nib, scl,
-                         N, K, Q, n_tiles, y);
-      break;
-    default:
-      hipLaunchKernelGGL(w4_gemv_kernel<1>, dim3(n_tiles), block, 0, st, xp, m, nib, scl, N, K, Q,
-                         n_tiles, y);
-      break;
+  const dim3 block(kGemvThreads);
+  if (per <= 4) {
+    const int per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
+    const dim3 grid(std::max(1, std::min(n_groups, 256 * per_cu)));
+    switch (per) {
+      case 1:
+        hipLaunchKernelGGL(w4_gemv_short_kernel<1>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
+        break;
+      case 2:
+        hipLaunchKernelGGL(w4_gemv_short_kernel<2>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
+        break;
+      case 3:
+        hipLaunchKernelGGL(w4_gemv_short_kernel<3>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
+        break;
+      default:
+        hipLaunchKernelGGL(w4_gemv_short_kernel<4>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
+        break;
+    }
+  } else {
+    hipLaunchKernelGGL(w4_gemv_long_kernel, dim3(n_groups), block, 0, st, xp, m, nib, scl, N, K, Q,
+                       n_tiles, y);
   }
   return hipGetLastError();
 }
@@ -406,7 +600,8 @@ hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int
   const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
   const size_t eb = w4_packed_bytes(N, K);
   const size_t scale_off = (size_t)n_tiles * Q * 1024;
-  const dim3 grid(n_tiles, m * topk);
+  const int tpw = kGemvWaves / gemv_ks(Q);
+  const dim3 grid((n_tiles + tpw - 1) / tpw, m * topk);
   hipLaunchKernelGGL(w4_gemv_routed_kernel<1>, grid, dim3(kGemvThreads), 0, st,
                      (const uint16_t*)x, x_per_slot, m, ids, topk, (const uint8_t*)packed_all, eb,
                      scale_off, E, N, K, Q, n_tiles, y);

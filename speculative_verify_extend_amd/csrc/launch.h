@@ -12,7 +12,7 @@ hipError_t launch_w4_pack(const uint8_t* w, const uint16_t* s, int N, int K, voi
                           hipStream_t st);
 hipError_t launch_w4_dequant(const void* packed, int N, int K, float* out, hipStream_t st);
 hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K, float* y,
-                          hipStream_t st, int nt_override);
+                          hipStream_t st, int wgs_per_cu);
 hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int32_t* ids,
                                  int topk, const void* packed_all, int E, int N, int K, float* y,
                                  hipStream_t st);
@@ -57,6 +57,11 @@ hipError_t launch_attn_combine(const AttnParams& p, hipStream_t st);
 // copy rows [start, start+len) of one slot/layer back to [len][Hkv][D] (test export)
 hipError_t launch_kv_read(const uint16_t* K, const uint16_t* Vt, int Hkv, int D, int cap,
                           int start, int len, uint16_t* k_out, uint16_t* v_out, hipStream_t st);
+
+// ---- measurement probes ------------------------------------------------------------
+hipError_t launch_probe_read(const void* src, size_t bytes, int blocks, int unroll, void* sink,
+                             hipStream_t st);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t st);
 
 // ---- slot matcher ----------------------------------------------------------------
 constexpr int kMaxLcpPairs = 16;

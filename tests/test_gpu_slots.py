@@ -102,3 +102,23 @@ def test_select_rejects_bad_prompts():
     with pytest.raises(sve.SveError) as e:
         st.kv_slot_select(np.zeros(129, np.int32))
     assert e.value.code == -3
+
+
+def test_batch_placement_before_prefill():
+    """Four prompts selected before one batched extend land in four slots,
+    as in the oracle; the rotation then reuses each slot's history."""
+    order = synth.rotation_sessions(9, 4, 3, 100, 7, 24, 36)
+    st = sve.KVSlots(4, 1, HQ, HKV, D, 1024, 1024)
+    o = SlotOracle(4)
+    announce("batch placement")
+    for rnd in range(3):
+        reqs = [p for _, p in order[4 * rnd:4 * rnd + 4]]
+        got = [st.kv_slot_select(p) for p in reqs]
+        want = [o.select(p) for p in reqs]
+        assert got == want
+        assert len({s for s, _ in got}) == 4
+        for (s, r), p in zip(got, reqs):
+            _fill(st, s, len(p))
+            o.extend(s, 0, len(p) - o.kv_len[s][0])
+        if rnd:
+            assert all(r > 0 for _, r in got)

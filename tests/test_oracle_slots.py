@@ -150,3 +150,13 @@ def test_truncate_then_extend_refills():
         o.extend(0, 1, 1)
     with pytest.raises(ValueError):
         o.truncate(0, 13)        # layer 0 holds only 12 rows
+
+
+def test_selected_slot_is_claimed_before_prefill():
+    """Prompts placed before any prefill get distinct slots: a slot handed to
+    a conversation is no longer empty ('How it works': a new conversation
+    takes an empty slot, else the least recently used one)."""
+    o = SlotOracle(4)
+    got = [o.select(np.array([9, 9, 9, s, s])) for s in range(4)]
+    assert got == [(0, 0), (1, 0), (2, 0), (3, 0)]
+    assert o.select(np.array([9, 9, 9, 7])) == (0, 0)   # LRU; nothing resident yet
