@@ -50,4 +50,15 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// max over lanes l, l^16, l^32, l^48 with the gfx950 row-swap permutes:
+// permlane32_swap(x, x) leaves (x[l % 32], x[l % 32 + 32]) in its two
+// results and permlane16_swap(x, x) the two 16-lane rows of each half, so
+// one max per step combines the partner lanes without going through LDS.
+__device__ __forceinline__ float max4_rows(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 }  // namespace sve

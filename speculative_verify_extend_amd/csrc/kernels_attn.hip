@@ -27,6 +27,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// 2^x by the hardware exponential (v_exp_f32); results below the normal
+// range flush to zero, which only ever affects probabilities that round to
+// nothing next to the row maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct SegRef {
   int s, local;
 };
@@ -80,32 +85,56 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
     const int d = c / kAppendRows, r = c % kAppendRows;
     if (r < rows) Vt[(size_t)d * cap + sg.P + i0 + r] = tile[d][r];
   }
+  // Positions after the sequence up to the end of its last 64-key tile are
+  // read by the attention kernels (with zero probability): keep them zero so
+  // stale cache contents can never reach the value product.
+  if (blockIdx.x == 0) {
+    const int e0 = sg.P + sg.m, e1 = min(cap, (e0 + 63) / 64 * 64);
+    for (int c = threadIdx.x; c < D * 64; c += 256) {
+      const int d = c >> 6, pos = e0 + (c & 63);
+      if (pos < e1) Vt[(size_t)d * cap + pos] = 0;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path. Workgroup = 4 waves; each wave owns RT tiles of 16 packed rows,
-// so a workgroup covers 64*RT packed rows of one KV head and one key split.
-// Per 64-key tile, K [64][D] and Vt [D][64] are staged once in LDS (double
-// buffered through registers) and shared by the four waves.
+// MFMA path. Workgroup = 8 waves in two key groups of 4. Both groups hold the
+// same 64*RT packed rows of one KV head (each wave 16*RT rows); group G takes
+// the 64-key tiles kstart + 64*(2j + G) of the workgroup's key split, so two
+// waves share every SIMD and one's matrix work overlaps the other's softmax.
+// Each group stages its tiles with direct global-to-LDS loads into its own
+// double buffer (K [64][D] and Vt [D][64], dense with an XOR swizzle of the
+// 16-byte chunks applied on the global side), requesting tile j+1 while
+// computing tile j. At the end group 1 hands its (max, sum, O) to group 0
+// through LDS and group 0 merges and writes.
 //   S^T = K Q^T   (A = 16 keys x 32 d from LDS, B = Q^T held in registers)
 //   O^T += Vt P^T (A = 16 d x 32 keys from LDS, B = P^T straight from the
 //                  S^T accumulators, rounded to bf16)
 // Within a 32-key chunk the 16-key MFMA sub-tiles take keys
 // 8*(j/4) + 4*sub + j%4, so that lane (row, kb) ends up holding keys
-// 8*kb .. 8*kb+7 of the chunk: exactly its B operand for the PV product, and
-// its Vt A operand is then one 16-byte LDS read. Each lane owns one packed
-// row (lane % 16): the online-softmax row statistics need only two cross-lane
-// steps (lanes l, l^16, l^32, l^48 hold the same row).
+// 8*kb .. 8*kb+7 of the chunk: exactly its B operand for the value product,
+// and its Vt A operand is one 16-byte LDS read. Each lane owns one packed
+// row (lane % 16): row statistics need two cross-lane steps only.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// swizzled 16-byte chunk position of chunk c in K-tile row `key` (D/8 chunks
+// per row) and in Vt-tile row `d` (8 chunks per row)
+template <int D>
+__device__ __forceinline__ int kswz(int key, int c) {
+  constexpr int CPR = D / 8;
+  return c ^ (((key & (CPR - 1)) ^ (((key >> 4) & 1) << 2)) & (CPR - 1));
+}
+__device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
+
 template <int D, int RT>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
+__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   constexpr int DC = D / 32;
   constexpr int DT = D / 16;
-  constexpr int KS = D + 8;   // LDS row stride of the K tile (bf16)
-  constexpr int VS = 64 + 8;  // LDS row stride of the Vt tile (bf16)
-  constexpr int KCH = (64 * D / 8) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VS];
+  constexpr int CPR = D / 8;            // 16-byte chunks per K row
+  constexpr int TILE = 64 * D;          // bf16 elements per K (or Vt) tile
+  constexpr int DMA_PER_WAVE = (TILE * 2) / 1024 / 4;  // 1 KB DMA steps per wave per tile part
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][2][TILE];  // [group][buf][K|Vt]
 
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   const SegRef ref = find_seg(prm, L);
@@ -118,6 +147,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
   const int P = sg.P, m = sg.m, R = m * g;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave >> 2, gw = wave & 3;
   const int kb = lane >> 4, col = lane & 15;
 
   const int wg_row0 = rb * 64 * RT;
@@ -126,13 +156,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
   const int kend = min(P + wg_last / g + 1, kstart + sg.split_keys);
   if (kstart >= kend) return;  // no row of this block sees this split
   const int wg_min_lim = P + wg_row0 / g;
+  const int ntiles = (kend - kstart + 63) / 64;
+  const int niter = (ntiles + 1) / 2;  // tile pairs
 
   int lim[RT], qi[RT], qh[RT];
   bool rvalid[RT];
   bf16x8 qreg[RT][DC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int pr = wg_row0 + wave * 16 * RT + 16 * rt + col;
+    const int pr = wg_row0 + gw * 16 * RT + 16 * rt + col;
     rvalid[rt] = pr < R;
     const int i = rvalid[rt] ? pr / g : 0;
     qi[rt] = i;
@@ -156,53 +188,36 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
 
   const uint16_t* Kg = sg.K + (size_t)kvh * cap * D;
   const uint16_t* Vg = sg.Vt + (size_t)kvh * D * cap;
-  const int kv_end = P + m;
   const float cs = prm.c;
 
-  u32x4 kst[KCH], vst[KCH];
-  auto gload = [&](int kt) {
+  // per-lane element offsets of the direct loads (fixed for every tile)
+  int koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = threadIdx.x + 256 * u;
-      const int row = c / (D / 8), cc = c % (D / 8);
-      kst[u] = load16(Kg + (size_t)(kt + row) * D + cc * 8);
-      const int d = c >> 3, kc = c & 7;
-      vst[u] = load16(Vg + (size_t)d * cap + kt + kc * 8);
-    }
-  };
-  // Loaded values are only touched here, a full tile of compute after the
-  // loads were issued: V at positions past the sequence is zeroed so stale
-  // cache contents can never reach the value product.
-  auto swrite = [&](int buf, int kt) {
+  for (int u = 0; u < DMA_PER_WAVE; ++u) {
+    const int pos = (gw + 4 * u) * 64 + lane;  // 16-byte chunk index within the tile part
+    const int key = pos / CPR, d = pos >> 3;
+    koff[u] = key * D + kswz<D>(key, pos % CPR) * 8;
+    voff[u] = d * cap + vswz(d, pos & 7) * 8;
+  }
+  // direct loads of tile `t` of this group into buffer `b`
+  auto dma = [&](int t, int b) {
+    const int kt = kstart + 64 * (2 * t + grp);
+    const uint16_t* kb_ = Kg + (size_t)kt * D;
+    const uint16_t* vb_ = Vg + kt;
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = threadIdx.x + 256 * u;
-      const int row = c / (D / 8), cc = c % (D / 8);
-      store16(&Ks[buf][row * KS + cc * 8], kst[u]);
-      const int d = c >> 3, kc = c & 7;
-      u32x4 v = vst[u];
-      const int key0 = kt + kc * 8;
-      if (key0 + 8 > kv_end) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t w = v[e];
-          w = (key0 + 2 * e >= kv_end) ? (w & 0xFFFF0000u) : w;
-          w = (key0 + 2 * e + 1 >= kv_end) ? (w & 0x0000FFFFu) : w;
-          v[e] = w;
-        }
-      }
-      store16(&Vs[buf][d * VS + kc * 8], v);
+    for (int u = 0; u < DMA_PER_WAVE; ++u) {
+      const int step = gw + 4 * u;  // 1 KB step within the tile part
+      __builtin_amdgcn_global_load_lds((const void*)(kb_ + koff[u]),
+                                       (lds_void*)&lds[grp][b][0][step * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb_ + voff[u]),
+                                       (lds_void*)&lds[grp][b][1][step * 512], 16, 0, 0);
     }
   };
 
-  gload(kstart);
-  swrite(0, kstart);
-  __syncthreads();
-  int buf = 0;
-  for (int kt = kstart; kt < kend; kt += 64) {
-    const bool more = kt + 64 < kend;
-    if (more) gload(kt + 64);
-
+  auto compute = [&](int t, int b) {
+    const int kt = kstart + 64 * (2 * t + grp);
+    const uint16_t* Ks = lds[grp][b][0];
+    const uint16_t* Vs = lds[grp][b][1];
     f32x4 S[RT][2][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -217,14 +232,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
         const int kappa = 32 * c + 8 * (col >> 2) + 4 * sub + (col & 3);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          const bf16x8 kop = as_bf16x8(load16(&Ks[buf][kappa * KS + 32 * dc + 8 * kb]));
+          const bf16x8 kop =
+              as_bf16x8(load16(Ks + kappa * D + kswz<D>(kappa, 4 * dc + kb) * 8));
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
             S[rt][c][sub] = mfma16x16x32(kop, qreg[rt][dc], S[rt][c][sub]);
         }
       }
     }
-
     // Keys past a row's causal limit only occur in tiles that reach beyond
     // the smallest limit of the workgroup's rows.
     const bool edge = kt + 63 > wg_min_lim;
@@ -248,19 +263,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
             }
             mx = fmaxf(mx, v);
           }
-      mx = fmaxf(mx, xor_shfl(mx, 16));
-      mx = fmaxf(mx, xor_shfl(mx, 32));
+      mx = max4_rows(mx);
       mcand[rt] = mx * cs;
       // the reference max moves only when a row's max grows by more than 8
       // (log2 units): probabilities then stay below 2^8 and the running
       // output is rescaled rarely
       grow |= mcand[rt] > mref[rt] + 8.f;
     }
-    if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
+    if (__ballot(grow) != 0) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const float mnew = fmaxf(mref[rt], mcand[rt]);
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mref[rt] - mnew);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mref[rt] - mnew);
         mref[rt] = mnew;
         lrun[rt] *= alpha;
 #pragma unroll
@@ -280,8 +294,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {
-            const float p0 = exp2f(fmaf(S[rt][c][sub][i], cs, -muse));
-            const float p1 = exp2f(fmaf(S[rt][c][sub][i + 1], cs, -muse));
+            const float p0 = fast_exp2(fmaf(S[rt][c][sub][i], cs, -muse));
+            const float p1 = fast_exp2(fmaf(S[rt][c][sub][i + 1], cs, -muse));
             const uint32_t w = pack_bf16x2(p0, p1);
             pk[2 * sub + (i >> 1)] = w;
             psum = dot2_bf16(w, 0x3F803F80u, psum);  // + both bf16 values exactly
@@ -290,22 +304,61 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams prm) {
       }
       lrun[rt] = psum;
     }
-
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + col;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 vop =
-            as_bf16x8(load16(&Vs[buf][(16 * dt + col) * VS + 32 * c + 8 * kb]));
+        const bf16x8 vop = as_bf16x8(load16(Vs + d * 64 + vswz(d, 4 * c + kb) * 8));
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) O[rt][dt] = mfma16x16x32(vop, pb[rt][c], O[rt][dt]);
       }
     }
+  };
 
-    if (more) swrite(buf ^ 1, kt + 64);
+  // group G owns tiles 0 .. mytiles-1 of its own sequence
+  const int mytiles = (ntiles - grp + 1) / 2;
+  if (mytiles > 0) dma(0, 0);
+  __syncthreads();
+  for (int j = 0; j < niter; ++j) {
+    if (j + 1 < mytiles) dma(j + 1, (j + 1) & 1);
+    if (j < mytiles) compute(j, j & 1);
     __syncthreads();
-    buf ^= 1;
   }
+
+  // merge group 1 into group 0 (same lane = same rows and columns)
+  float* xo = reinterpret_cast<float*>(&lds[0][0][0][0]);  // 256 lanes x (RT*(DT*4 + 2))
+  constexpr int PER = RT * (DT * 4 + 2);
+  const int gl = gw * 64 + lane;
+  if (grp == 1) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      xo[(rt * (DT * 4 + 2) + 0) * 256 + gl] = mref[rt];
+      xo[(rt * (DT * 4 + 2) + 1) * 256 + gl] = lrun[rt];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xo[(rt * (DT * 4 + 2) + 2 + dt * 4 + i) * 256 + gl] = O[rt][dt][i];
+    }
+  }
+  __syncthreads();
+  if (grp == 1) return;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float m1 = xo[(rt * (DT * 4 + 2) + 0) * 256 + gl];
+    const float l1 = xo[(rt * (DT * 4 + 2) + 1) * 256 + gl];
+    const float M = fmaxf(mref[rt], m1);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float s0 = fast_exp2(mref[rt] - Mu), s1 = fast_exp2(m1 - Mu);
+    lrun[rt] = lrun[rt] * s0 + l1 * s1;
+    mref[rt] = M;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        O[rt][dt][i] = O[rt][dt][i] * s0 + xo[(rt * (DT * 4 + 2) + 2 + dt * 4 + i) * 256 + gl] * s1;
+  }
+  (void)PER;
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -454,9 +507,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
         const float mx = wave_max(s);
         const float mnew = fmaxf(mrun[r], mx * cs);
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(mrun[r] - muse);
+        const float alpha = fast_exp2(mrun[r] - muse);
         mrun[r] = mnew;
-        const float p = exp2f(fmaf(s, cs, -muse));
+        const float p = fast_exp2(fmaf(s, cs, -muse));
         const uint32_t pw = pack_bf16x2(p, 0.f) & 0xFFFFu;
         lrun[r] = lrun[r] * alpha + bf16_to_f32(pw);
         // key-adjacent pairs of p: lane 2t holds the low half, 2t+1 the high
@@ -505,7 +558,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
     float o = 0.f, l = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float sc = exp2f(wm[w][r] - Mu);
+      const float sc = fast_exp2(wm[w][r] - Mu);
       o += sc * wo[w][r][d];
       l += sc * wl[w][r];
     }
@@ -545,24 +598,35 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   if (sg.splits == 1) return;
   const int i = grow - sg.row_begin;
   const int nvalid = min(sg.splits, (sg.P + i) / sg.split_keys + 1);
-  float M = -INFINITY;
-  for (int sp = 0; sp < nvalid; ++sp)
-    M = fmaxf(M, sg.ws_ml[(((size_t)sp * sg.m + i) * p.Hq + h) * 2]);
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  for (int sp = 0; sp < nvalid; ++sp) {
-    const float* ml = sg.ws_ml + (((size_t)sp * sg.m + i) * p.Hq + h) * 2;
-    const float sc = exp2f(ml[0] - M);
-    l += sc * ml[1];
-    const f32x4 v =
-        *reinterpret_cast<const f32x4*>(sg.ws_o + (((size_t)sp * sg.m + i) * p.Hq + h) * D + c4);
+  // all loads first (one round trip), then the fixed-order merge
+  float2 ml[16];
+  f32x4 o[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] += sc * v[e];
+  for (int sp = 0; sp < 16; ++sp) {
+    const int q = min(sp, nvalid - 1);
+    const size_t r = ((size_t)q * sg.m + i) * p.Hq + h;
+    ml[sp] = *reinterpret_cast<const float2*>(sg.ws_ml + r * 2);
+    o[sp] = *reinterpret_cast<const f32x4*>(sg.ws_o + r * D + c4);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp)
+    if (sp < nvalid) M = fmaxf(M, ml[sp].x);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < 16; ++sp) {
+    if (sp < nvalid) {
+      const float sc = fast_exp2(ml[sp].x - M);
+      l += sc * ml[sp].y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += sc * o[sp][e];
+    }
   }
   const float inv = 1.f / l;
   u32x2 w;
-  w[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
-  w[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+  w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<u32x2*>(sg.out + ((size_t)i * p.Hq + h) * D + c4) = w;
 }
 
@@ -607,9 +671,9 @@ hipError_t launch_attn(const AttnParams& p, int path, hipStream_t st) {
       hipLaunchKernelGGL(attn_valu_kernel<64>, grid, block, 0, st, p);
   } else {
     if (p.D == 128)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(512), 0, st, p);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(512), 0, st, p);
   }
   return hipGetLastError();
 }
