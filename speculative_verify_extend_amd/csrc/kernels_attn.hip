@@ -16,6 +16,8 @@
 // Work is split over key ranges ("splits") aligned to absolute multiples of
 // the split length; each split yields an unnormalised partial (O, running
 // max, sum) merged afterwards in a fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     }
   };
 
-  auto compute = [&](int t, int b) {
+  auto compute = [&](int t, int b, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int kt = kstart + 64 * (2 * t + grp);
     const uint16_t* Ks = lds[grp][b][0];
     const uint16_t* Vs = lds[grp][b][1];
@@ -240,9 +243,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         }
       }
     }
-    // Keys past a row's causal limit only occur in tiles that reach beyond
-    // the smallest limit of the workgroup's rows.
-    const bool edge = kt + 63 > wg_min_lim;
     bf16x8 pb[RT][2];
     bool grow = false;
     float mcand[RT];
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float v = S[rt][c][sub][i];
-            if (edge) {
+            if constexpr (EDGE) {
               const int key = kt + 32 * c + 8 * kb + 4 * sub + i;
               v = (key <= lim[rt]) ? v : -INFINITY;
               S[rt][c][sub][i] = v;
@@ -322,43 +322,46 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   __syncthreads();
   for (int j = 0; j < niter; ++j) {
     if (j + 1 < mytiles) dma(j + 1, (j + 1) & 1);
-    if (j < mytiles) compute(j, j & 1);
+    if (j < mytiles) {
+      // Keys past a row's causal limit only occur in tiles that reach beyond
+      // the smallest limit of the workgroup's rows; only those tiles mask.
+      const int kt = kstart + 64 * (2 * j + grp);
+      if (kt + 63 > wg_min_lim)
+        compute(j, j & 1, std::true_type{});
+      else
+        compute(j, j & 1, std::false_type{});
+    }
     __syncthreads();
   }
 
   // merge group 1 into group 0 (same lane = same rows and columns)
-  float* xo = reinterpret_cast<float*>(&lds[0][0][0][0]);  // 256 lanes x (RT*(DT*4 + 2))
-  constexpr int PER = RT * (DT * 4 + 2);
+  f32x4* xo = reinterpret_cast<f32x4*>(&lds[0][0][0][0]);  // [RT*(DT+1)][256 lanes]
   const int gl = gw * 64 + lane;
   if (grp == 1) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      xo[(rt * (DT * 4 + 2) + 0) * 256 + gl] = mref[rt];
-      xo[(rt * (DT * 4 + 2) + 1) * 256 + gl] = lrun[rt];
+      xo[(rt * (DT + 1)) * 256 + gl] = f32x4{mref[rt], lrun[rt], 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xo[(rt * (DT * 4 + 2) + 2 + dt * 4 + i) * 256 + gl] = O[rt][dt][i];
+      for (int dt = 0; dt < DT; ++dt) xo[(rt * (DT + 1) + 1 + dt) * 256 + gl] = O[rt][dt];
     }
   }
   __syncthreads();
   if (grp == 1) return;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float m1 = xo[(rt * (DT * 4 + 2) + 0) * 256 + gl];
-    const float l1 = xo[(rt * (DT * 4 + 2) + 1) * 256 + gl];
-    const float M = fmaxf(mref[rt], m1);
+    const f32x4 ml1 = xo[(rt * (DT + 1)) * 256 + gl];
+    const float M = fmaxf(mref[rt], ml1[0]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
-    const float s0 = fast_exp2(mref[rt] - Mu), s1 = fast_exp2(m1 - Mu);
-    lrun[rt] = lrun[rt] * s0 + l1 * s1;
+    const float s0 = fast_exp2(mref[rt] - Mu), s1 = fast_exp2(ml1[0] - Mu);
+    lrun[rt] = lrun[rt] * s0 + ml1[1] * s1;
     mref[rt] = M;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 o1 = xo[(rt * (DT + 1) + 1 + dt) * 256 + gl];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        O[rt][dt][i] = O[rt][dt][i] * s0 + xo[(rt * (DT * 4 + 2) + 2 + dt * 4 + i) * 256 + gl] * s1;
+      for (int i = 0; i < 4; ++i) O[rt][dt][i] = O[rt][dt][i] * s0 + o1[i] * s1;
+    }
   }
-  (void)PER;
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
