@@ -363,7 +363,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the GEMV / verify / MoE / slot sweeps")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run the copy probe (256 MiB, three times): the known byte count "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.calibrate:
+        torch.cuda.set_device(0)
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            sve.probe_copy(src, dst, 4096)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": src.numel(), "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is not sharded); got --gpus {args.gpus}",
               file=sys.stderr)

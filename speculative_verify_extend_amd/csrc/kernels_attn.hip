@@ -201,9 +201,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     koff[u] = key * D + kswz<D>(key, pos % CPR) * 8;
     voff[u] = d * cap + vswz(d, pos & 7) * 8;
   }
+  // Row blocks walk their tiles from different starting points (rotated by
+  // the row block index), so the workgroups sharing a KV head do not all
+  // fetch the same tile from L2 at the same moment.
+  const int mytiles = (ntiles - grp + 1) / 2;  // tiles of this key group
+  auto tile_kt = [&](int t) { return kstart + 64 * (2 * ((t + rb) % max(mytiles, 1)) + grp); };
   // direct loads of tile `t` of this group into buffer `b`
   auto dma = [&](int t, int b) {
-    const int kt = kstart + 64 * (2 * t + grp);
+    const int kt = tile_kt(t);
     const uint16_t* kb_ = Kg + (size_t)kt * D;
     const uint16_t* vb_ = Vg + kt;
 #pragma unroll
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
 
   auto compute = [&](int t, int b, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const int kt = kstart + 64 * (2 * t + grp);
+    const int kt = tile_kt(t);
     const uint16_t* Ks = lds[grp][b][0];
     const uint16_t* Vs = lds[grp][b][1];
     f32x4 S[RT][2][2];
@@ -317,7 +322,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   };
 
   // group G owns tiles 0 .. mytiles-1 of its own sequence
-  const int mytiles = (ntiles - grp + 1) / 2;
   if (mytiles > 0) dma(0, 0);
   __syncthreads();
   for (int j = 0; j < niter; ++j) {
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     if (j < mytiles) {
       // Keys past a row's causal limit only occur in tiles that reach beyond
       // the smallest limit of the workgroup's rows; only those tiles mask.
-      const int kt = kstart + 64 * (2 * j + grp);
+      const int kt = tile_kt(j);
       if (kt + 63 > wg_min_lim)
         compute(j, j & 1, std::true_type{});
       else

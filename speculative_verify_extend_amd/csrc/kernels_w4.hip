@@ -308,7 +308,7 @@ __device__ __forceinline__ void gemv_group_store(float (*red)[4][64], f32x4& acc
   __syncthreads();
 }
 
-template <int QPW>
+template <int QPW, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void w4_gemv_short_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
     const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
@@ -360,6 +360,14 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_short_kernel(
   // The scheduling fences keep each buffer's loads contiguous in issue order
   // on every path into the loop, so the wait before consuming a buffer only
   // covers that buffer.
+  if constexpr (SINGLE) {
+    // one tile group per workgroup: a single buffer, no second pipeline stage
+    ShortBuf<QPW> A;
+    issue(g0, A);
+    consume(A);
+    gemv_group_store(red, acc, KS, TPW, g0 * TPW, true, n_tiles, m, N, y);
+    return;
+  }
   ShortBuf<QPW> A, B;
   issue(g0, A);
   __builtin_amdgcn_sched_barrier(0);
@@ -571,22 +579,24 @@ hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K
   const uint16_t* xp = (const uint16_t*)x;
   const dim3 block(kGemvThreads);
   if (per <= 4) {
+    // up to two workgroups per CU: one tile group each; beyond that a
+    // persistent grid of one workgroup per CU walks runs of tile groups
+    const bool single = wgs_per_cu <= 0 && n_groups <= 2 * 256;
     const int per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
-    const dim3 grid(std::max(1, std::min(n_groups, 256 * per_cu)));
-    switch (per) {
-      case 1:
-        hipLaunchKernelGGL(w4_gemv_short_kernel<1>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
-        break;
-      case 2:
-        hipLaunchKernelGGL(w4_gemv_short_kernel<2>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
-        break;
-      case 3:
-        hipLaunchKernelGGL(w4_gemv_short_kernel<3>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
-        break;
-      default:
-        hipLaunchKernelGGL(w4_gemv_short_kernel<4>, grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y);
-        break;
+    const dim3 grid(single ? n_groups : std::max(1, std::min(n_groups, 256 * per_cu)));
+#define SVE_SHORT(Q_, S_) \
+  hipLaunchKernelGGL((w4_gemv_short_kernel<Q_, S_>), grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y)
+    switch (per * 2 + (single ? 1 : 0)) {
+      case 2: SVE_SHORT(1, false); break;
+      case 3: SVE_SHORT(1, true); break;
+      case 4: SVE_SHORT(2, false); break;
+      case 5: SVE_SHORT(2, true); break;
+      case 6: SVE_SHORT(3, false); break;
+      case 7: SVE_SHORT(3, true); break;
+      case 8: SVE_SHORT(4, false); break;
+      default: SVE_SHORT(4, true); break;
     }
+#undef SVE_SHORT
   } else {
     hipLaunchKernelGGL(w4_gemv_long_kernel, dim3(n_groups), block, 0, st, xp, m, nib, scl, N, K, Q,
                        n_tiles, y);

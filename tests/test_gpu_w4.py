@@ -48,16 +48,18 @@ def test_gemv_matches_oracle(m, n, k):
     assert err.max() <= GEMV_TOL, err
 
 
-@pytest.mark.parametrize("nt", [1, 2, 4])
-def test_gemv_tile_grouping_is_invisible(nt, monkeypatch):
-    """Workgroups owning 1, 2 or 4 row tiles give bitwise the same output."""
-    n, k, m = 1000, 1024, 5
-    announce(f"gemv nt={nt}")
+@pytest.mark.parametrize("wpc", [1, 2])
+@pytest.mark.parametrize("n,k", [(1000, 1024), (4096, 4096), (640, 12288)])
+def test_gemv_launch_forms_agree_bitwise(n, k, wpc, monkeypatch):
+    """One-group-per-workgroup launches and persistent launches (1 or 2
+    workgroups per CU) give bitwise the same output."""
+    m = 5
+    announce(f"gemv forms n={n} k={k} wpc={wpc}")
     w, s, packed = _weights(4, n, k)
     x = dev_bf16(synth.normal_bf16(synth.rng(5), (m, k)))
-    monkeypatch.setenv("SVE_GEMV_NT", "1")
+    monkeypatch.delenv("SVE_GEMV_WGS_PER_CU", raising=False)
     ref = sve.w4_gemv_m(x, packed, n, k).cpu()
-    monkeypatch.setenv("SVE_GEMV_NT", str(nt))
+    monkeypatch.setenv("SVE_GEMV_WGS_PER_CU", str(wpc))
     got = sve.w4_gemv_m(x, packed, n, k).cpu()
     assert torch.equal(ref, got)
 
