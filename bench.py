@@ -2,6 +2,7 @@
 """Benchmark of the extend-prefill / m-row int4 GEMV hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+                    [--no-graph] [--layers L] [--calibrate]
 
 Timed step (the headline): one turn of the agent-turn replay at turn 9 on a
 7B-like attention layer (28 q / 4 KV heads, head_dim 128): truncate the slot
@@ -9,21 +10,31 @@ back to the 1668 cached tokens, select the slot for the 1922-token prompt
 (reuses 1668), then extend 254 new rows in each of 128 attention layers. 128
 layers are rotated so that the 500 MB of KV read per step cannot sit in the
 256 MB Infinity Cache. value = 254 new tokens per attention-layer pass / time
-of one pass (step time / 128).
+of one pass (step time / 128), the per-layer calls replayed from a captured
+HIP graph.
+
+The roofline object is for the step's dominant kernel, the extend attention
+kernel: its duration is taken from HIP events that the library records on its
+stream around that kernel in every call of the eager timed steps.
 
 Also measured in the same run and reported beside it: the m-row int4 GEMV
-(9B-like and 7B-like layers, m = 1..8, weights rotated over 8 copies), the
-speculative-verify attention sweep (2048 cached + m rows), the routed MoE
-GEMV (256 experts, top-8), and four slots in rotation (batched extend).
-Inputs are seeded synthetic data with the workloads' shapes, resident in HBM
-before timing starts. The CPU oracle is timed on a bounded sample.
+(9B-like and 7B-like layers, m = 1..8, weights rotated over 8 copies, each
+launch bracketed by HIP events, and a plain streaming read of the same
+buffers as the achievable floor), the speculative-verify attention sweep
+(2048 cached + m rows), the routed MoE GEMV (256 experts, top-8), and four
+slots in rotation (batched extend). Inputs are seeded synthetic data with the
+workloads' shapes, resident in HBM before timing starts. The CPU oracle is
+timed on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -40,6 +51,10 @@ METRIC = "extend-prefill tok/s at 1668+254 ctx; m-row int4 GEMV GB/s vs HBM peak
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 ROT_LAYERS = 128
+# counter summary of the attention kernel at the headline workload, and the
+# sources whose hash it records (a changed kernel makes its traffic stale)
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_mfma_replay7b_turn9_traffic.md")
+ATTN_SOURCES = ["kernels_attn.hip", "common.h", "launch.h"]
 
 
 def bf16_dev(bits):
@@ -68,6 +83,97 @@ class Timer:
         self.ms = self.a.elapsed_time(self.b)
 
 
+class Backlog:
+    """A long streaming read queued ahead of eagerly launched calls, so that
+    the host is ahead of the GPU and each bracketed kernel starts as soon as
+    its predecessor ends."""
+
+    def __init__(self, nbytes=1 << 30):
+        self.buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        sve.probe_read(self.buf, 1024, 1)
+
+
+class HipEvents:
+    """Timing events of the HIP runtime torch has loaded, created without a
+    system-scope fence (hipEventDisableSystemFence): a default event writes
+    back and invalidates caches when it is recorded, and that time would be
+    counted as part of the bracketed kernel."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP status {rc}")
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._ok(self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS), "hipEventCreate")
+            evs.append(e)
+        return evs
+
+    def record(self, e):
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self._ok(self.hip.hipEventRecord(e, s), "hipEventRecord")
+
+    def elapsed(self, a, b):
+        f = ctypes.c_float()
+        self._ok(self.hip.hipEventElapsedTime(ctypes.byref(f), a, b), "hipEventElapsedTime")
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+_EVENTS = None
+
+
+def bracket(calls, backlog):
+    """Per-call durations (ms) from HIP events recorded on the current
+    stream right before and after each call (one kernel each)."""
+    global _EVENTS
+    if _EVENTS is None:
+        _EVENTS = HipEvents()
+    ev = _EVENTS.create(2 * len(calls))
+    torch.cuda.synchronize()
+    backlog()
+    for i, f in enumerate(calls):
+        _EVENTS.record(ev[2 * i])
+        f()
+        _EVENTS.record(ev[2 * i + 1])
+    torch.cuda.synchronize()
+    out = [_EVENTS.elapsed(ev[2 * i], ev[2 * i + 1]) for i in range(len(calls))]
+    _EVENTS.destroy(ev)
+    return out
+
+
+def graph_of(fn, reset=lambda: None, stream=None):
+    """Capture fn's launches in a HIP graph (one eager run first; reset()
+    restores the host state before each)."""
+    reset()
+    fn()
+    torch.cuda.synchronize()
+    reset()
+    stream = stream or torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def attn_flops(P, m, hq, d):
     return 4 * d * hq * (m * P + m * (m + 1) // 2)
 
@@ -86,6 +192,30 @@ def fit(ms, ts):
     b = ((m - m.mean()) * (t - t.mean())).sum() / ((m - m.mean()) ** 2).sum()
     a = t.mean() - b * m.mean()
     return float(a), float(b)
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "speculative_verify_extend_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_summary():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]+)`", text, flags=re.M))
+    if fields.get("source_sha256") != attn_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------------------
@@ -128,62 +258,63 @@ class Replay:
             self.out.append(torch.empty_like(q))
         torch.cuda.synchronize()
 
-    def step(self):
+    def select(self):
         self.st.kv_truncate(0, self.P)
         slot, r = self.st.kv_slot_select(self.p_turn)
         assert (slot, r) == (0, self.P), (slot, r)
+
+    def extend_all(self):
         for layer in range(self.layers):
             self.st.extend_attn(0, layer, self.q[layer], self.k[layer], self.v[layer], self.out[layer])
+
+    def step(self, backlog=None):
+        self.select()
+        if backlog:
+            backlog()
+        self.extend_all()
 
     def capture(self):
         """Capture the per-layer extend calls of one step in a HIP graph
         (torch's graph capture records the library's launches on the capture
         stream). Replays repeat exactly these kernels: the step's KV rows are
         rewritten in place, so a replay after truncate + select is one turn."""
-        self.stream = torch.cuda.Stream()
+        self.select()
+        stream = torch.cuda.Stream()
         self.graph = torch.cuda.CUDAGraph()
-        self.st.kv_truncate(0, self.P)
-        self.st.kv_slot_select(self.p_turn)
         torch.cuda.synchronize()
-        with torch.cuda.graph(self.graph, stream=self.stream):
-            for layer in range(self.layers):
-                self.st.extend_attn(0, layer, self.q[layer], self.k[layer], self.v[layer],
-                                    self.out[layer])
+        with torch.cuda.graph(self.graph, stream=stream):
+            self.extend_all()
         torch.cuda.synchronize()
 
     def step_graph(self):
-        self.st.kv_truncate(0, self.P)
-        slot, r = self.st.kv_slot_select(self.p_turn)
-        assert (slot, r) == (0, self.P), (slot, r)
+        self.select()
         self.graph.replay()
 
-    def time_extend_graph(self, reps=5):
-        best = math.inf
-        for _ in range(reps):
-            with Timer() as t:
-                self.graph.replay()
-            best = min(best, t.ms / self.layers)
-        return best
 
-    def time_extend_only(self, reps=3):
-        """Average duration of one extend call (append + attention kernels)."""
-        best = math.inf
-        for _ in range(reps):
-            self.st.kv_truncate(0, self.P)
-            self.st.kv_slot_select(self.p_turn)
-            with Timer() as t:
-                for layer in range(self.layers):
-                    self.st.extend_attn(0, layer, self.q[layer], self.k[layer], self.v[layer],
-                                        self.out[layer])
-            best = min(best, t.ms / self.layers)
-        return best
+# ---------------------------------------------------------------------------
+# measured HBM ceilings
+# ---------------------------------------------------------------------------
+
+def hbm_probe(backlog):
+    """Plain streaming read (1 GiB) and copy (2 x 512 MiB) of device memory."""
+    buf = backlog.buf
+    read = min(bracket([lambda: sve.probe_read(buf, 1024, 1)] * 3, backlog))
+    half = buf.numel() // 2
+    src, dst = buf[:half], buf[half:]
+    copy = min(bracket([lambda: sve.probe_copy(src, dst, 2048)] * 3, backlog))
+    return {"read_GBps": round(buf.numel() / (read * 1e-3) / 1e9, 1),
+            "copy_GBps": round(2 * half / (copy * 1e-3) / 1e9, 1),
+            "what": "streaming read of 1 GiB and copy of 512 MiB, HIP events per launch"}
 
 
 # ---------------------------------------------------------------------------
 # GEMV sweep
 # ---------------------------------------------------------------------------
 
-def gemv_sweep(shapes, copies=8, reps=5, m_values=range(1, 9), seed=3):
+def gemv_sweep(shapes, backlog, copies=8, m_values=range(1, 9), seed=3, reps=3):
+    """Per m: each matrix's launches bracketed by HIP events (median over the
+    rotated copies and repeats), the layer's sum, and a plain read of the
+    same packed buffers (the floor a weight-streaming kernel can reach)."""
     g = synth.rng(seed, 55)
     mats = []
     for (n, k) in shapes:
@@ -193,33 +324,37 @@ def gemv_sweep(shapes, copies=8, reps=5, m_values=range(1, 9), seed=3):
         mats.append((n, k, packs))
         del wd, sd
     kmax = max(k for _, k in shapes)
-    nmax = max(n for n, _ in shapes)
     xs = [bf16_dev(synth.normal_bf16(g, (8, kmax))) for _ in range(copies)]
-    ys = [torch.empty((8, nmax), dtype=torch.float32, device="cuda") for _ in range(copies)]
+    floors = {}
+    for (n, k, packs) in mats:
+        best = math.inf
+        for blocks, unroll in ((1024, 2), (2048, 2), (512, 4)):
+            d = []
+            for _ in range(reps):
+                d += bracket([lambda p=p: sve.probe_read(p, blocks, unroll) for p in packs], backlog)
+            best = min(best, float(np.median(d)))
+        floors[(n, k)] = best
     res = {}
     for m in m_values:
-        # inputs and outputs per copy, prepared before timing
-        xsl = {}
-        for c in range(copies):
-            for (n, k, _) in mats:
-                xsl[(c, k)] = xs[c][:m, :k].contiguous()
-        ysl = {}
-        for c in range(copies):
-            for (n, k, _) in mats:
-                ysl[(c, n)] = torch.empty((m, n), dtype=torch.float32, device="cuda")
-
-        def run2():
-            for c in range(copies):
-                for (n, k, packs) in mats:
-                    sve.w4_gemv_m(xsl[(c, k)], packs[c], n, k, ysl[(c, n)])
-        run2()
-        best = math.inf
-        for _ in range(reps):
-            with Timer() as t:
-                run2()
-            best = min(best, t.ms / copies)
-        nbytes = sum(gemv_bytes(m, n, k) for (n, k, _) in mats)
-        res[m] = dict(us=best * 1e3, GBps=nbytes / (best * 1e-3) / 1e9, bytes=nbytes)
+        per = {}
+        for (n, k, packs) in mats:
+            xk = [x[:m, :k].contiguous() for x in xs]
+            ys = [torch.empty((m, n), dtype=torch.float32, device="cuda") for _ in range(copies)]
+            calls = [lambda c=c: sve.w4_gemv_m(xk[c], packs[c], n, k, ys[c]) for c in range(copies)]
+            for f in calls:
+                f()
+            d = []
+            for _ in range(reps):
+                d += bracket(calls, backlog)
+            t = float(np.median(d))
+            nb = gemv_bytes(m, n, k)
+            per[f"{n}x{k}"] = dict(us=t * 1e3, GBps=nb / (t * 1e-3) / 1e9, bytes=nb,
+                                   floor_us=floors[(n, k)] * 1e3)
+        us = sum(v["us"] for v in per.values())
+        nbytes = sum(v["bytes"] for v in per.values())
+        floor = sum(v["floor_us"] for v in per.values())
+        res[m] = dict(us=us, GBps=nbytes / (us * 1e-6) / 1e9, bytes=nbytes, floor_us=floor,
+                      per_matrix=per)
     return res
 
 
@@ -227,7 +362,7 @@ def gemv_sweep(shapes, copies=8, reps=5, m_values=range(1, 9), seed=3):
 # verify attention sweep (9B-like, 2048 cached)
 # ---------------------------------------------------------------------------
 
-def verify_sweep(layers=ROT_LAYERS, reps=3):
+def verify_sweep(backlog, layers=ROT_LAYERS, reps=3, graphs=True):
     wl = synth.WORKLOADS["verify9b"]
     hq, hkv, d, P = wl["hq"], wl["hkv"], wl["d"], wl["context"]
     st = sve.KVSlots(1, layers, hq, hkv, d, P + 64, P)
@@ -242,15 +377,34 @@ def verify_sweep(layers=ROT_LAYERS, reps=3):
     for m in range(1, 9):
         qm, km, vm = q[:m].contiguous(), k[:m].contiguous(), v[:m].contiguous()
         out = torch.empty_like(qm)
-        best = math.inf
-        for _ in range(reps):
-            st.kv_truncate(0, P)
-            with Timer() as t:
-                for layer in range(layers):
-                    st.extend_attn(0, layer, qm, km, vm, out)
-            best = min(best, t.ms / layers)
-        res[m] = dict(us=best * 1e3,
-                      GBps=attn_bytes(P, m, hq, hkv, d) / (best * 1e-3) / 1e9)
+
+        def run():
+            for layer in range(layers):
+                st.extend_attn(0, layer, qm, km, vm, out)
+        # kernel durations from the library's events (eager)
+        st.kv_truncate(0, P)
+        st.timing_start(layers)
+        torch.cuda.synchronize()
+        backlog()
+        run()
+        kt = st.timing_read()
+        r = dict(attn_kernel_us=kt["attn_ms"] / kt["calls"] * 1e3,
+                 append_kernel_us=kt["append_ms"] / kt["calls"] * 1e3,
+                 combine_kernel_us=kt["combine_ms"] / kt["calls"] * 1e3)
+        if graphs:
+            gr = graph_of(run, reset=lambda: st.kv_truncate(0, P))
+            best = math.inf
+            for _ in range(reps):
+                st.kv_truncate(0, P)
+                with Timer() as t:
+                    gr.replay()
+                best = min(best, t.ms / layers)
+            r["call_us"] = best * 1e3
+            del gr
+        st.kv_truncate(0, P)
+        r["GBps_attn_kernel"] = attn_bytes(P, m, hq, hkv, d) / (r["attn_kernel_us"] * 1e-6) / 1e9
+        res[m] = r
+    st.close()
     return res
 
 
@@ -258,7 +412,7 @@ def verify_sweep(layers=ROT_LAYERS, reps=3):
 # MoE routed GEMV (35B-A3B-like)
 # ---------------------------------------------------------------------------
 
-def moe_sweep(reps=3, n_routings=16, sets=2):
+def moe_sweep(backlog, n_routings=16, sets=2):
     wl = synth.WORKLOADS["moe35b"]
     E, hid, f, topk = wl["n_experts"], wl["hidden"], wl["expert_ffn"], wl["topk"]
     n1, k1, n2, k2 = 2 * f, hid, hid, f
@@ -281,21 +435,18 @@ def moe_sweep(reps=3, n_routings=16, sets=2):
         h = bf16_dev(synth.normal_bf16(g, (m, topk, k2)))
         y1 = torch.empty((m, topk, n1), dtype=torch.float32, device="cuda")
         y2 = torch.empty((m, topk, n2), dtype=torch.float32, device="cuda")
-
-        def run():
-            for i in range(n_routings):
-                s = i % sets
-                sve.w4_gemv_m_routed(x, ids[i], W1[s], E, n1, k1, False, y1)
-                sve.w4_gemv_m_routed(h, ids[i], W2[s], E, n2, k2, True, y2)
-        run()
-        best = math.inf
-        for _ in range(reps):
-            with Timer() as t:
-                run()
-            best = min(best, t.ms / n_routings)
+        up = [lambda i=i: sve.w4_gemv_m_routed(x, ids[i], W1[i % sets], E, n1, k1, False, y1)
+              for i in range(n_routings)]
+        down = [lambda i=i: sve.w4_gemv_m_routed(h, ids[i], W2[i % sets], E, n2, k2, True, y2)
+                for i in range(n_routings)]
+        for fn in up + down:
+            fn()
+        tu = bracket(up, backlog)
+        td = bracket(down, backlog)
+        us = (sum(tu) + sum(td)) / n_routings * 1e3
         ub = float(np.mean(union)) * (eb1 + eb2)
-        res[m] = dict(us=best * 1e3, union_experts=float(np.mean(union)),
-                      GBps=ub / (best * 1e-3) / 1e9)
+        res[m] = dict(us=us, up_us=float(np.median(tu)) * 1e3, down_us=float(np.median(td)) * 1e3,
+                      union_experts=float(np.mean(union)), GBps=ub / (us * 1e-6) / 1e9)
     return res
 
 
@@ -303,15 +454,14 @@ def moe_sweep(reps=3, n_routings=16, sets=2):
 # four slots in rotation (4B-like), batched extend
 # ---------------------------------------------------------------------------
 
-def slots_rotation():
+def slots_rotation(backlog):
     wl = synth.WORKLOADS["slots4b"]
     hq, hkv, d = wl["hq"], wl["hkv"], wl["d"]
     st = sve.KVSlots(4, 1, hq, hkv, d, 1024, 4 * 1024)
     order = synth.rotation_sessions(wl["seed"], 4, wl["turns"], wl["state_tokens"],
                                     wl["shared_start"], wl["question_min"], wl["question_max"])
     g = synth.rng(wl["seed"], 88)
-    prefilled, times, toks = [], [], 0
-    # first round: fill the four 800+ token states
+    prefilled, kern, toks = [], [], 0
     for rnd in range(wl["turns"]):
         reqs = order[4 * rnd:4 * rnd + 4]
         sel = [st.kv_slot_select(p) for _, p in reqs]
@@ -319,14 +469,18 @@ def slots_rotation():
         prefilled.append(ms)
         total = sum(ms)
         q, k, v = (bf16_dev(a) for a in synth.attention_rows(g, total, hq, hkv, d))
-        with Timer() as t:
-            st.extend_attn_batched([s for s, _ in sel], ms, 0, q, k, v)
-        if rnd > 0:
-            times.append(t.ms)
+        st.timing_start(1)
+        torch.cuda.synchronize()
+        backlog()
+        st.extend_attn_batched([s for s, _ in sel], ms, 0, q, k, v)
+        kt = st.timing_read()
+        if rnd > 0:  # the first round fills the 800-token states
+            kern.append(kt["append_ms"] + kt["attn_ms"] + kt["combine_ms"])
             toks += total
+    st.close()
     return dict(prefilled_per_turn=prefilled,
-                batched_tok_per_s=toks / (sum(times) * 1e-3) if times else None,
-                ms_per_round=float(np.median(times)) if times else None)
+                batched_tok_per_s=toks / (sum(kern) * 1e-3) if kern else None,
+                kernel_ms_per_round=float(np.median(kern)) if kern else None)
 
 
 # ---------------------------------------------------------------------------
@@ -355,6 +509,14 @@ def cpu_baseline(case, P, budget_s=10.0):
                        f"new rows, fp64 numpy), repeated {n}x over {budget_s:.0f} s")
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def r2(v):
+    return round(float(v), 2)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,13 +524,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the GEMV / verify / MoE / slot sweeps")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the headline from eager launches only (for counter runs)")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the copy probe (256 MiB, three times): the known byte count "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is not sharded); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    sve.load_library()
     if args.calibrate:
-        torch.cuda.set_device(0)
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -376,46 +545,62 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel(), "launches": 3}))
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the path is not sharded); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    sve.load_library()
 
-    print("[bench] replay setup", file=sys.stderr, flush=True)
+    backlog = Backlog()
+    log("replay setup")
     rp = Replay(args.layers)
-    # eager: every layer's extend launched from Python
     for _ in range(args.warmup):
         rp.step()
     torch.cuda.synchronize()
-    with Timer() as t:
-        for _ in range(args.steps):
-            rp.step()
-    ms_eager = t.ms / args.steps
-    # graph: the same calls captured once and replayed
-    rp.capture()
-    for _ in range(args.warmup):
-        rp.step_graph()
-    torch.cuda.synchronize()
-    with Timer() as t:
-        for _ in range(args.steps):
+    # eager steps: every layer's extend launched from Python; the library
+    # records events around each call's kernels
+    rp.st.timing_start(args.steps * args.layers)
+    ms_eager = 0.0
+    for _ in range(args.steps):
+        rp.select()
+        backlog()
+        with Timer() as t:
+            rp.extend_all()
+        ms_eager += t.ms
+    kt = rp.st.timing_read()
+    ms_eager /= args.steps
+    calls = kt["calls"]
+    attn_us = kt["attn_ms"] / calls * 1e3
+    append_us = kt["append_ms"] / calls * 1e3
+    combine_us = kt["combine_ms"] / calls * 1e3
+    if args.no_graph:
+        ms_step = ms_eager
+    else:
+        # graph: the same calls captured once and replayed
+        rp.capture()
+        for _ in range(args.warmup):
             rp.step_graph()
-    ms_step = t.ms / args.steps
+        torch.cuda.synchronize()
+        ms_step = 0.0
+        for _ in range(args.steps):
+            rp.select()
+            with Timer() as t:
+                rp.graph.replay()
+            ms_step += t.ms
+        ms_step /= args.steps
     per_layer_s = ms_step * 1e-3 / args.layers
     value = rp.m / per_layer_s
-    print(f"[bench] step {ms_step:.3f} ms (eager {ms_eager:.3f}), {per_layer_s * 1e6:.2f} us per "
-          "layer", file=sys.stderr, flush=True)
+    log(f"step {ms_step:.3f} ms (eager {ms_eager:.3f}), {per_layer_s * 1e6:.2f} us per layer; "
+        f"kernels append {append_us:.2f} attn {attn_us:.2f} combine {combine_us:.2f} us")
 
-    ext_ms = rp.time_extend_graph()
     flops = attn_flops(rp.P, rp.m, rp.hq, rp.d)
-    achieved = flops / (ext_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+    achieved = flops / (attn_us * 1e-6) / 1e12
+    traffic = traffic_from_summary()
+    roofline = {"bound": "mfma", "achieved": r2(achieved), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None,
-                "kernel": "one extend call (kv_append + attn_mfma + combine kernels), 1668+254, "
-                          "28/4 heads, D 128, timed by HIP events over graph replays",
-                "us_per_launch": round(ext_ms * 1e3, 2), "flops_per_launch": flops}
+                "traffic": traffic,
+                "kernel": "attn_mfma_kernel<128> (extend attention, 1668 cached + 254 rows, "
+                          "28/4 heads, D 128)",
+                "us_per_launch": r2(attn_us), "flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": attn_bytes(rp.P, rp.m, rp.hq, rp.hkv, rp.d),
+                "timing": "HIP events recorded by the library on its stream around the kernel, "
+                          f"averaged over {calls} eager calls",
+                "other_kernels_us": {"kv_append": r2(append_us), "combine": r2(combine_us)}}
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tok/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -423,56 +608,72 @@ def main():
            "data": "synthetic",
            "config": {"workload": "agent-turn replay turn 9: select + extend of 254 new rows over "
                                   "1668 cached, 7B-like attention layer (28 q / 4 KV heads, D 128), "
-                                  f"{args.layers} layers rotated, per-layer calls replayed from a "
-                                  "captured HIP graph; value = tokens per layer pass",
-                      "global_batch": rp.m, "seq_len": rp.n, "parallelism": "none",
+                                  f"{args.layers} layers rotated, per-layer calls "
+                                  + ("launched eagerly" if args.no_graph else
+                                     "replayed from a captured HIP graph")
+                                  + "; value = new tokens per layer pass",
+                      "new_rows": rp.m, "cached": rp.P, "layers": args.layers,
                       "ms_per_step_eager": round(ms_eager, 4)},
            "roofline": roofline}
 
     if not args.no_extra:
-        print("[bench] gemv sweep", file=sys.stderr, flush=True)
-        g9 = gemv_sweep(synth.layer_gemv_shapes(4096, 12288, 32, 8, 128))
-        g7 = gemv_sweep(synth.layer_gemv_shapes(3584, 18944, 28, 4, 128), copies=6, m_values=(1, 4, 8))
+        log("hbm probe")
+        out["hbm_probe"] = hbm_probe(backlog)
+        log("gemv sweep")
+        g9 = gemv_sweep(synth.layer_gemv_shapes(4096, 12288, 32, 8, 128), backlog)
+        g7 = gemv_sweep(synth.layer_gemv_shapes(3584, 18944, 28, 4, 128), backlog, copies=6,
+                        m_values=(1, 4, 8))
         a, b = fit(list(g9), [g9[m]["us"] for m in g9])
         worst = min(v["GBps"] for v in g9.values())
         out["gemv"] = {
             "workload": "9B-like layer (QKV 6144x4096, O 4096x4096, gate|up 24576x4096, "
-                        "down 4096x12288), int4 group-32, 8 rotated copies",
-            "GBps_min_over_m": round(worst, 1), "frac_of_hbm_peak_min": round(worst / HBM_PEAK_GBS, 4),
-            "per_m": {m: {"us": round(v["us"], 2), "GBps": round(v["GBps"], 1),
-                          "frac": round(v["GBps"] / HBM_PEAK_GBS, 4)} for m, v in g9.items()},
-            "fit_us": {"fixed": round(a, 3), "per_row": round(b, 3), "per_row_over_fixed": round(b / a, 4)},
-            "7b_layer_per_m": {m: {"us": round(v["us"], 2), "GBps": round(v["GBps"], 1)} for m, v in g7.items()},
+                        "down 4096x12288), int4 group-32, 8 rotated copies; per-launch kernel "
+                        "time from HIP events; layer = sum of the four launches",
+            "roofline": {"bound": "hbm", "achieved": round(worst, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(worst / HBM_PEAK_GBS, 4),
+                         "what": "worst m of 1..8, algorithmic bytes / summed kernel time"},
+            "per_m": {m: {"us": r2(v["us"]), "GBps": round(v["GBps"], 1),
+                          "frac": round(v["GBps"] / HBM_PEAK_GBS, 4),
+                          "read_floor_us": r2(v["floor_us"]),
+                          "per_matrix_us": {kk: r2(pv["us"]) for kk, pv in v["per_matrix"].items()}}
+                      for m, v in g9.items()},
+            "read_floor_per_matrix_us": {kk: r2(pv["floor_us"])
+                                         for kk, pv in g9[1]["per_matrix"].items()},
+            "fit_us": {"fixed": round(a, 3), "per_row": round(b, 3),
+                       "per_row_over_fixed": round(b / a, 4)},
+            "7b_layer_per_m": {m: {"us": r2(v["us"]), "GBps": round(v["GBps"], 1)}
+                               for m, v in g7.items()},
         }
-        print("[bench] verify sweep", file=sys.stderr, flush=True)
-        vs = verify_sweep(layers=min(args.layers, ROT_LAYERS))
-        a2, b2 = fit(list(vs), [vs[m]["us"] for m in vs])
+        log("verify sweep")
+        vs = verify_sweep(backlog, layers=min(args.layers, ROT_LAYERS))
+        a2, b2 = fit(list(vs), [vs[m]["attn_kernel_us"] for m in vs])
         out["verify_attention"] = {
             "workload": "9B-like attention (32 q / 8 KV heads, D 128), 2048 cached + m rows",
-            "per_m": {m: {"us": round(v["us"], 2), "GBps": round(v["GBps"], 1)} for m, v in vs.items()},
-            "fit_us": {"fixed": round(a2, 3), "per_row": round(b2, 3)}}
+            "per_m": {m: {kk: r2(vv) for kk, vv in v.items()} for m, v in vs.items()},
+            "fit_attn_kernel_us": {"fixed": round(a2, 3), "per_row": round(b2, 3)}}
         # the same sweep with each kernel path forced, as evidence for the
         # default path choice
         for path, rows in (("valu", "100000"), ("mfma", "1")):
             os.environ["SVE_MFMA_MIN_ROWS"] = rows
-            vp = verify_sweep(layers=32, reps=2)
-            out["verify_attention"]["forced_" + path] = {m: round(v["us"], 2) for m, v in vp.items()}
+            vp = verify_sweep(backlog, layers=32, graphs=False)
+            out["verify_attention"]["forced_" + path + "_attn_kernel_us"] = {
+                m: r2(v["attn_kernel_us"]) for m, v in vp.items()}
         os.environ.pop("SVE_MFMA_MIN_ROWS", None)
-        print("[bench] moe sweep", file=sys.stderr, flush=True)
-        mo = moe_sweep()
+        log("moe sweep")
+        mo = moe_sweep(backlog)
         a3, b3 = fit(list(mo), [mo[m]["us"] for m in mo])
         out["moe"] = {
             "workload": "35B-A3B-like expert layer: 256 experts, W1 1024x2048, W2 2048x512, top-8",
-            "per_m": {m: {"us": round(v["us"], 2), "union_experts": round(v["union_experts"], 2),
+            "per_m": {m: {"us": r2(v["us"]), "union_experts": r2(v["union_experts"]),
                           "GBps": round(v["GBps"], 1)} for m, v in mo.items()},
             "fit_us": {"fixed": round(a3, 3), "per_row": round(b3, 3)}}
-        print("[bench] slots", file=sys.stderr, flush=True)
-        out["slots"] = slots_rotation()
+        log("slots")
+        out["slots"] = slots_rotation(backlog)
 
     if not args.no_cpu:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(rp.case, rp.P)
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -200,6 +200,21 @@ int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll
                    void* hip_stream);
 int sve_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* hip_stream);
 
+/* ---- kernel timing (measurement aid) -------------------------------------
+ * sve_timing_start makes the next n_calls extend calls on ctx record HIP
+ * timing events on the context stream around each of their three kernels
+ * (KV append, attention, split combine); the events are created by the
+ * library without a system-scope fence, so they add no cache write-back to
+ * the timed kernels. sve_timing_read waits for the last recorded event, writes the
+ * summed durations in milliseconds of each kernel over the timed calls and
+ * their count, destroys the events and ends timing (a combine that a call
+ * does not need counts as 0). Not for calls under graph capture.
+ *   1 <= n_calls <= 65536. Errors: SVE_E_ARG, SVE_E_STATE (start while
+ *   started, read while not started), SVE_E_HIP. */
+int sve_timing_start(sve_ctx* ctx, int32_t n_calls);
+int sve_timing_read(sve_ctx* ctx, float* append_ms, float* attn_ms, float* combine_ms,
+                    int32_t* calls);
+
 /* Message for a status code. */
 const char* sve_strerror(int code);
 

@@ -138,6 +138,17 @@ class KVSlots:
             _ptr(out)), self.ctx)
         return out
 
+    def timing_start(self, n_calls: int) -> None:
+        """Record HIP events around the kernels of the next n_calls extend calls."""
+        check(self._lib.sve_timing_start(self.ctx, int(n_calls)), self.ctx)
+
+    def timing_read(self) -> dict:
+        """Summed kernel durations (ms) of the timed extend calls; ends timing."""
+        a, b, c, n = C.c_float(), C.c_float(), C.c_float(), C.c_int32()
+        check(self._lib.sve_timing_read(self.ctx, C.byref(a), C.byref(b), C.byref(c), C.byref(n)),
+              self.ctx)
+        return {"append_ms": a.value, "attn_ms": b.value, "combine_ms": c.value, "calls": n.value}
+
     def kv_read(self, slot: int, layer: int, start: int, length: int):
         """Cached K and V rows [start, start+length) as bf16 [length][Hkv][D]."""
         k = torch.empty((length, self.hkv, self.d), dtype=torch.bfloat16, device=self.arena.device)

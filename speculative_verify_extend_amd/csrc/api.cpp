@@ -90,6 +90,10 @@ struct sve_ctx {
   std::vector<long long> tick;
   long long clock;
   std::string err;
+  // kernel timing: 4 events per timed extend call (before the KV append,
+  // after it, after the attention kernel, after the combine kernel)
+  std::vector<hipEvent_t> tev;
+  int timed_max = 0, timed_used = 0;
 
   int32_t* tok() { return (int32_t*)(arena + lay.off_tok); }
   int32_t* slot_tok(int s) { return (int32_t*)(arena + lay.off_slot_tok) + (size_t)s * lay.cap; }
@@ -220,12 +224,18 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
   }
   int path = kPathMfma;
   plan_attention(c, p, path);
+  hipEvent_t* ev = nullptr;
+  if (c->timed_used < c->timed_max) ev = &c->tev[4 * (size_t)c->timed_used++];
+  if (ev) SVE_HIP(c, hipEventRecord(ev[0], c->stream));
   hipError_t e = launch_kv_append(p, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "kv_append launch");
+  if (ev) SVE_HIP(c, hipEventRecord(ev[1], c->stream));
   e = launch_attn(p, path, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "extend_attn launch");
+  if (ev) SVE_HIP(c, hipEventRecord(ev[2], c->stream));
   e = launch_attn_combine(p, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "combine launch");
+  if (ev) SVE_HIP(c, hipEventRecord(ev[3], c->stream));
   for (int i = 0; i < n; ++i) c->kv_len[slots[i]][layer] += ms[i];
   return SVE_OK;
 }
@@ -278,7 +288,54 @@ int sve_create(const sve_config* cfg, void* arena, size_t arena_bytes, void* hip
 
 int sve_destroy(sve_ctx* ctx) {
   if (!ctx) return fail(nullptr, SVE_E_ARG, "null context");
+  for (hipEvent_t e : ctx->tev) (void)hipEventDestroy(e);
   delete ctx;
+  return SVE_OK;
+}
+
+int sve_timing_start(sve_ctx* c, int32_t n_calls) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  if (n_calls < 1 || n_calls > 65536) return fail(c, SVE_E_ARG, "n_calls must be 1..65536");
+  if (c->timed_max) return fail(c, SVE_E_STATE, "timing already started");
+  c->tev.assign(4 * (size_t)n_calls, nullptr);
+  for (size_t i = 0; i < c->tev.size(); ++i) {
+    // no system-scope fence at the events: a cache write-back there would be
+    // timed as part of the neighbouring kernels
+    hipError_t e = hipEventCreateWithFlags(&c->tev[i], hipEventDisableSystemFence);
+    if (e != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(c->tev[j]);
+      c->tev.clear();
+      return hip_fail(c, e, "hipEventCreate");
+    }
+  }
+  c->timed_max = n_calls;
+  c->timed_used = 0;
+  return SVE_OK;
+}
+
+int sve_timing_read(sve_ctx* c, float* append_ms, float* attn_ms, float* combine_ms,
+                    int32_t* calls) {
+  if (!c) return fail(nullptr, SVE_E_ARG, "null context");
+  if (!append_ms || !attn_ms || !combine_ms || !calls) return fail(c, SVE_E_ARG, "null pointer");
+  if (!c->timed_max) return fail(c, SVE_E_STATE, "timing was not started");
+  double acc[3] = {0, 0, 0};
+  hipError_t err = hipSuccess;
+  if (c->timed_used > 0) err = hipEventSynchronize(c->tev[4 * (size_t)c->timed_used - 1]);
+  for (int i = 0; i < c->timed_used && err == hipSuccess; ++i)
+    for (int k = 0; k < 3 && err == hipSuccess; ++k) {
+      float ms = 0.f;
+      err = hipEventElapsedTime(&ms, c->tev[4 * (size_t)i + k], c->tev[4 * (size_t)i + k + 1]);
+      acc[k] += ms;
+    }
+  const int used = c->timed_used;
+  for (hipEvent_t e : c->tev) (void)hipEventDestroy(e);
+  c->tev.clear();
+  c->timed_max = c->timed_used = 0;
+  if (err != hipSuccess) return hip_fail(c, err, "reading timing events");
+  *append_ms = (float)acc[0];
+  *attn_ms = (float)acc[1];
+  *combine_ms = (float)acc[2];
+  *calls = used;
   return SVE_OK;
 }
 

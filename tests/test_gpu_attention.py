@@ -223,3 +223,30 @@ def test_batched_matches_single_slot_calls():
         assert np.abs(part - want).max() <= ATTN_TOL
         assert np.abs(part - single).max() <= ATTN_TOL
         row += ms[i]
+
+
+def test_kernel_timing_records_each_call():
+    """Timing events around the three kernels of each timed call: positive
+    attention time, a count capped at the requested calls, state errors, and
+    results unchanged by timing."""
+    hq, hkv, d, P, m = 28, 4, 128, 600, 40
+    c = synth.attention_case(11, hq, hkv, d, P, m)
+    st = _store(hq, hkv, d, P + m + 64, P + m)
+    st.kv_slot_select(np.arange(P + m, dtype=np.int32))
+    st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]), dev_bf16(c["v_prefix"]))
+    q, k, v = dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"])
+    announce("kernel timing")
+    ref = st.extend_attn(0, 0, q, k, v)
+    with pytest.raises(sve.SveError) as e:
+        st.timing_read()
+    assert e.value.code == -5
+    st.timing_start(3)
+    with pytest.raises(sve.SveError):
+        st.timing_start(3)
+    for _ in range(5):
+        st.kv_truncate(0, P)
+        assert torch.equal(st.extend_attn(0, 0, q, k, v), ref)
+    t = st.timing_read()
+    assert t["calls"] == 3
+    assert t["attn_ms"] > 0 and t["append_ms"] > 0 and t["combine_ms"] >= 0
+    assert t["attn_ms"] < 3 * 10.0  # milliseconds: a sanity bound, not a speed check

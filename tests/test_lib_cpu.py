@@ -81,4 +81,7 @@ def test_null_context_is_rejected(lib):
     assert lib.sve_kv_truncate(None, 0, 0) == _lib.SVE_E_ARG
     assert lib.sve_extend_attn(None, 0, 0, None, None, None, 1, None) == _lib.SVE_E_ARG
     assert lib.sve_destroy(None) == _lib.SVE_E_ARG
+    assert lib.sve_timing_start(None, 4) == _lib.SVE_E_ARG
+    f, i = C.c_float(), C.c_int32()
+    assert lib.sve_timing_read(None, C.byref(f), C.byref(f), C.byref(f), C.byref(i)) == _lib.SVE_E_ARG
     assert lib.sve_strerror(_lib.SVE_E_STATE) == b"call out of order"
