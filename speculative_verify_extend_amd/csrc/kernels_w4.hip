@@ -22,6 +22,7 @@
 // every lane exactly the B operand of four v_mfma_f32_16x16x32_bf16 (one per
 // group). Rows past N and groups past K/32 are padded with code 8 and scale 0.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.h"
 #include "launch.h"
@@ -241,44 +242,55 @@ __device__ __forceinline__ void gemv_reduce(GemvAcc<NT>& acc, int KS, int tiles,
   }
 }
 
-// Choose the k-slice count: 8 slices when there are at least 8 quads, fewer
-// (and more tile lanes per workgroup) for short K.
+// Choose the k-slice count of the routed kernel: 8 slices when there are at
+// least 8 quads, fewer (and more tile lanes per workgroup) for short K.
 __host__ __device__ inline int gemv_ks(int Q) { return Q >= 8 ? 8 : Q >= 4 ? 4 : Q >= 2 ? 2 : 1; }
 
-// Dense m-row GEMV. Two straight-line pipelines (no data-dependent branches
-// around loads, so the compiler's wait counts stay exact and loads overlap):
+// ---------------------------------------------------------------------------
+// Dense m-row GEMV.
 //
-//  * short K (at most four quads per wave slice): a grid of about one
-//    workgroup per CU walks a contiguous run of tile groups (TPW = 8/KS row
-//    tiles each). Each wave loads the activation operands of its k slice
-//    once (live rows only) and double-buffers the weight/scale blocks of
-//    tile groups: the blocks of group g+2 are requested while group g is
-//    consumed.
-//  * long K: one tile group per workgroup; each wave walks its slice in
-//    chunks of four quads (weights, scales and activations), double
-//    buffered.
-// Steps past the end of a run or slice re-read a valid block and are
-// neutralised by a zero scale. After each tile group the KS partial sums are
-// added in LDS in a fixed order and stored.
+// A workgroup of W waves (W <= 16) owns a contiguous run of 16-row output
+// tiles; wave w owns a contiguous slice of the k quads and accumulates its
+// slice's contribution to every tile of the run. The slices' partial sums
+// are parked in LDS (one 1 KB slot per tile and wave, written without a
+// barrier) and added in a fixed wave order once per batch of tiles, so the
+// waves never wait for each other inside the weight stream and the result
+// does not depend on the launch shape.
+//
+// Instruction budget per 32-element group and 16 output rows: one wave-wide
+// 16-byte load per 4 groups, seven VALU ops to turn the group's nibble dword
+// into the MFMA B operand (bf16 128 + code), one fp16->fp32 scale
+// conversion, one v_mfma_f32_16x16x32_bf16 whose accumulator input is the
+// precomputed C0 = -136 * sum(x) of the group (so D = sum x * (code - 8)),
+// and four FMAs that apply the group scale. All addressing is wave-uniform
+// (scalar registers) plus a fixed per-lane offset.
+//
+//  * short K (one slice of at most QPW quads per wave covers K): the wave's
+//    activation operands and their C0 stay in registers for the whole run;
+//    tile blocks are double buffered.
+//  * long K: one tile per workgroup; each wave walks its slice two quads at
+//    a time with weights, scales and activations double buffered, C0 being
+//    computed per group.
+// Loads past the end of a run or slice re-read the last valid block (an L2
+// hit) so that no load sits under a data-dependent branch; their results
+// are discarded or scaled by zero.
+// ---------------------------------------------------------------------------
 
-template <int QPW>
-struct ShortBuf {
-  u32x4 w[QPW];
-  u32x2 s[QPW];
-};
+constexpr int kGemvMaxWaves = 16;
+constexpr int kGemvPartSlots = 128;  // 1 KB LDS slots for parked partial sums
 
-__device__ __forceinline__ void mfma_group(const bf16x8 a, uint32_t dw, float sc, bf16x8 neg136,
-                                           f32x4& acc) {
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  const f32x4 c0 = mfma16x16x32(a, neg136, zero4);
+// B operand of one group: lane dword dw holds 8 codes (element e at bit
+// 4*(e/2) for even e, 16 + 4*(e/2) for odd e); returns bf16 pairs 128+code.
+// Each pair is a shift and one gfx950 three-input bit operation
+// (v_bitop3_b32, truth table 0xEA = (src0 & src1) | src2).
+__device__ __forceinline__ bf16x8 w4_bfrag(uint32_t dw) {
+  constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x43004300u;
   u32x4 b;
-  b[0] = (dw & 0x000F000Fu) | 0x43004300u;
-  b[1] = ((dw >> 4) & 0x000F000Fu) | 0x43004300u;
-  b[2] = ((dw >> 8) & 0x000F000Fu) | 0x43004300u;
-  b[3] = ((dw >> 12) & 0x000F000Fu) | 0x43004300u;
-  const f32x4 d = mfma16x16x32(a, as_bf16x8(b), c0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, d[i], acc[i]);
+  b[0] = __builtin_amdgcn_bitop3_b32(dw, kMask, kExp, 0xEA);
+  b[1] = __builtin_amdgcn_bitop3_b32(dw >> 4, kMask, kExp, 0xEA);
+  b[2] = __builtin_amdgcn_bitop3_b32(dw >> 8, kMask, kExp, 0xEA);
+  b[3] = __builtin_amdgcn_bitop3_b32(dw >> 12, kMask, kExp, 0xEA);
+  return as_bf16x8(b);
 }
 
 __device__ __forceinline__ float scale_of(u32x2 sv, int j) {
@@ -286,108 +298,165 @@ __device__ __forceinline__ float scale_of(u32x2 sv, int j) {
   return f16_bits_to_f32((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
 }
 
-// Add the KS slices of one tile group in LDS and store the outputs.
-__device__ __forceinline__ void gemv_group_store(float (*red)[4][64], f32x4& acc, int KS, int TPW,
-                                                 int tile0, bool live, int n_tiles, int m, int N,
-                                                 float* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ bf16x8 neg136_operand() {
+  u32x4 m136;
+  m136[0] = m136[1] = m136[2] = m136[3] = 0xC308C308u;  // bf16(-136) x 8
+  return as_bf16x8(m136);
+}
+
+// One group: acc += sc * (MFMA(a, B(dw)) + c0).
+__device__ __forceinline__ void w4_group(bf16x8 a, f32x4 c0, uint32_t dw, float sc, f32x4& acc) {
+  const f32x4 d = mfma16x16x32(a, w4_bfrag(dw), c0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
-  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, d[i], acc[i]);
+}
+
+// Park a wave's partial sums of one tile in LDS slot `slot`.
+__device__ __forceinline__ void park(f32x4* part, int slot, const f32x4& acc) {
+  part[slot * 64 + (threadIdx.x & 63)] = acc;
+}
+
+// Add the W parked partials of tiles [tile0, tile0 + nt) in wave order and
+// store the live rows. Slot of (tile-in-batch tl, wave w) is tl * W + w.
+__device__ __forceinline__ void flush_tiles(const f32x4* part, int W, int tile0, int nt, int m,
+                                            int N, float* __restrict__ y) {
   __syncthreads();
-  if (live) {
-    for (int id = threadIdx.x; id < TPW * 256; id += kGemvThreads) {
-      const int l = id & 63, i = (id >> 6) & 3, tsi = id >> 8;
-      const int tile = tile0 + tsi;
-      float sum = red[tsi * KS][i][l];
-      for (int k2 = 1; k2 < KS; ++k2) sum += red[tsi * KS + k2][i][l];
-      const int row = 4 * (l >> 4) + i, n = 16 * tile + (l & 15);
-      if (tile < n_tiles && row < m && n < N) y[(size_t)row * N + n] = sum;
-    }
+  const float* pf = reinterpret_cast<const float*>(part);
+  for (int id = threadIdx.x; id < nt * 256; id += blockDim.x) {
+    const int i = id & 3, l = (id >> 2) & 63, tl = id >> 8;
+    const int row = 4 * (l >> 4) + i;
+    const int n = 16 * (tile0 + tl) + (l & 15);
+    if (row >= m || n >= N) continue;
+    float sum = 0.f;
+    for (int w = 0; w < W; ++w) sum += pf[((tl * W + w) * 64 + l) * 4 + i];
+    y[(size_t)row * N + n] = sum;
   }
   __syncthreads();
 }
 
-template <int QPW, bool SINGLE>
-__global__ __launch_bounds__(kGemvThreads) void w4_gemv_short_kernel(
+template <int QPW>
+struct TileBuf {
+  u32x4 w[QPW];
+  u32x2 s[QPW];
+};
+
+// waves per workgroup the short kernel allows for QPW quads per wave (its
+// register budget: activations and C0 of 4*QPW groups plus two tile buffers)
+__host__ __device__ constexpr int short_max_waves(int qpw) { return qpw <= 2 ? 16 : 8; }
+
+// HOIST: C0 of every group of the wave's slice is computed once and kept in
+// registers (one MFMA per group in the stream); otherwise it is recomputed
+// per group (two MFMAs per group, fewer registers).
+template <int QPW, bool SINGLE, bool HOIST>
+__global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
     const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
-  __shared__ float red[kGemvWaves][4][64];
-  const int KS = gemv_ks(Q), TPW = kGemvWaves / KS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ts = wave / KS, ksl = wave % KS, kb = lane >> 4, r = lane & 15;
-  const int n_groups = (n_tiles + TPW - 1) / TPW;
-  const int g0 = (int)((long long)blockIdx.x * n_groups / gridDim.x);
-  const int g1 = (int)((long long)(blockIdx.x + 1) * n_groups / gridDim.x);
-  if (g0 >= g1) return;
-  const int q0 = ksl * QPW;           // first quad of this wave's slice
-  const int nq = max(0, min(QPW, Q - q0));  // real quads in the slice
-  const bool xlive = r < m;
-  const uint16_t* xrow = x + (size_t)(xlive ? r : 0) * K;
-  u32x4 m136;
-  m136[0] = m136[1] = m136[2] = m136[3] = 0xC308C308u;
-  const bf16x8 neg136 = as_bf16x8(m136);
+  constexpr int SLOTS = SINGLE ? kGemvMaxWaves : kGemvPartSlots;
+  __shared__ f32x4 part[SLOTS * 64];
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, r = lane & 15;
+  const int G = K >> 5;
+  const int t0 = (int)((long long)blockIdx.x * n_tiles / gridDim.x);
+  const int t1 = (int)((long long)(blockIdx.x + 1) * n_tiles / gridDim.x);
+  const int q0 = wave * QPW;
+  const int nq = max(0, min(QPW, Q - q0));  // real quads of this wave (uniform)
+  const int batch = SLOTS / W;              // tiles per LDS batch
+  const bf16x8 neg136 = neg136_operand();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  u32x4 xr[QPW][4];
+  // activation operands (A row = input row r, rows past m repeat row m-1 and
+  // are never stored) and their C0 terms, once for the whole run
+  const uint16_t* xl = x + (size_t)min(r, m - 1) * K + 8 * kb;
+  bf16x8 xa[QPW][4];
+  f32x4 c0[HOIST ? QPW : 1][4];
 #pragma unroll
   for (int a = 0; a < QPW; ++a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      xr[a][j] = u32x4{0u, 0u, 0u, 0u};
-      if (xlive && a < nq) xr[a][j] = load16(xrow + min(128 * (q0 + a) + 32 * j + 8 * kb, K - 8));
+      const int g = min(4 * (q0 + a) + j, G - 1);
+      xa[a][j] = as_bf16x8(load16(xl + 32 * g));
     }
-
-  auto issue = [&](int g, ShortBuf<QPW>& b) {
-    const int tile = min(min(g, g1 - 1) * TPW + ts, n_tiles - 1);
+  // quads past K (the last wave of an uneven split re-reads a real block
+  // there) meet zero activations, so they add exactly zero
 #pragma unroll
-    for (int a = 0; a < QPW; ++a) {
-      const size_t blk = (size_t)tile * Q + min(q0 + a, Q - 1);
-      b.w[a] = load16(nib + blk * 1024 + lane * 16);
-      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + r * 8);
+  for (int a = 0; a < QPW; ++a)
+    if (a >= nq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xa[a][j] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  // C0 terms: computed once the activations arrive, after the first weight
+  // loads are in flight (the in-order load counter then waits for the
+  // activations only)
+  auto hoist_c0 = [&]() {
+    if constexpr (HOIST) {
+#pragma unroll
+      for (int a = 0; a < QPW; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c0[a][j] = mfma16x16x32(xa[a][j], neg136, zero4);
     }
   };
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](const ShortBuf<QPW>& b) {
+
+  const uint32_t loff = lane * 16, soff = r * 8;
+  auto issue = [&](int t, TileBuf<QPW>& b) {
+    t = min(t, t1 - 1);
+#pragma unroll
+    for (int a = 0; a < QPW; ++a) {
+      const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
+      b.w[a] = load16(nib + blk * 1024 + loff);
+      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+    }
+  };
+  auto consume = [&](const TileBuf<QPW>& b) {
+    f32x4 acc = zero4;
 #pragma unroll
     for (int a = 0; a < QPW; ++a)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sc = (a < nq) ? scale_of(b.s[a], j) : 0.f;
-        mfma_group(as_bf16x8(xr[a][j]), b.w[a][j], sc, neg136, acc);
+        const float sc = scale_of(b.s[a], j);
+        const f32x4 c = HOIST ? c0[HOIST ? a : 0][j] : mfma16x16x32(xa[a][j], neg136, zero4);
+        w4_group(xa[a][j], c, b.w[a][j], sc, acc);
       }
+    return acc;
   };
 
-  // The scheduling fences keep each buffer's loads contiguous in issue order
-  // on every path into the loop, so the wait before consuming a buffer only
-  // covers that buffer.
   if constexpr (SINGLE) {
-    // one tile group per workgroup: a single buffer, no second pipeline stage
-    ShortBuf<QPW> A;
-    issue(g0, A);
-    consume(A);
-    gemv_group_store(red, acc, KS, TPW, g0 * TPW, true, n_tiles, m, N, y);
+    TileBuf<QPW> A;
+    issue(t0, A);
+    hoist_c0();
+    park(part, wave, consume(A));
+    flush_tiles(part, W, t0, 1, m, N, y);
     return;
   }
-  ShortBuf<QPW> A, B;
-  issue(g0, A);
+  // double-buffered walk over the run; the fences keep each buffer's loads
+  // contiguous in issue order so the wait before a consume covers only it
+  TileBuf<QPW> A, B;
+  issue(t0, A);
   __builtin_amdgcn_sched_barrier(0);
-  issue(g0 + 1, B);
+  issue(t0 + 1, B);
   __builtin_amdgcn_sched_barrier(0);
-  for (int g = g0; g < g1; g += 2) {
-    consume(A);
+  hoist_c0();
+  int tb = t0;  // first tile of the current LDS batch
+  for (int t = t0; t < t1; t += 2) {
+    const f32x4 acc0 = consume(A);
     __builtin_amdgcn_sched_barrier(0);
-    issue(g + 2, A);
+    issue(t + 2, A);
     __builtin_amdgcn_sched_barrier(0);
-    gemv_group_store(red, acc, KS, TPW, g * TPW, true, n_tiles, m, N, y);
-    consume(B);
+    park(part, (t - tb) * W + wave, acc0);
+    const f32x4 acc1 = consume(B);
     __builtin_amdgcn_sched_barrier(0);
-    issue(g + 3, B);
+    issue(t + 3, B);
     __builtin_amdgcn_sched_barrier(0);
-    gemv_group_store(red, acc, KS, TPW, (g + 1) * TPW, g + 1 < g1, n_tiles, m, N, y);
+    if (t + 1 < t1) park(part, (t + 1 - tb) * W + wave, acc1);
+    const int done = min(t + 2, t1) - tb;
+    if (done + 2 > batch || t + 2 >= t1) {  // batch full (or run ends): add and store
+      flush_tiles(part, W, tb, done, m, N, y);
+      tb += done;
+    }
   }
 }
 
-constexpr int kLongChunk = 2;  // quads per chunk
+constexpr int kLongChunk = 2;  // quads per pipeline step
 
 struct LongBuf {
   u32x4 w[kLongChunk];
@@ -395,55 +464,61 @@ struct LongBuf {
   u32x4 x[kLongChunk][4];
 };
 
-__global__ __launch_bounds__(kGemvThreads) void w4_gemv_long_kernel(
+constexpr int kLongMaxWaves = 8;
+
+__global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
     const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
-  __shared__ float red[kGemvWaves][4][64];
-  const int KS = gemv_ks(Q), TPW = kGemvWaves / KS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ts = wave / KS, ksl = wave % KS, kb = lane >> 4, r = lane & 15;
-  const int g = blockIdx.x;
-  const int tile = min(g * TPW + ts, n_tiles - 1);
-  const int per = (Q + KS - 1) / KS;
-  const int q0 = ksl * per;
+  __shared__ f32x4 part[kGemvMaxWaves * 64];
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, r = lane & 15;
+  const int G = K >> 5;
+  const int tile = blockIdx.x;
+  const int per = (Q + W - 1) / W;
+  const int q0 = wave * per;
   const int nq = max(0, min(per, Q - q0));
   const int nchunks = (per + kLongChunk - 1) / kLongChunk;  // same for every wave
-  const bool xlive = r < m;
-  const uint16_t* xrow = x + (size_t)(xlive ? r : 0) * K;
-  u32x4 m136;
-  m136[0] = m136[1] = m136[2] = m136[3] = 0xC308C308u;
-  const bf16x8 neg136 = as_bf16x8(m136);
+  const bf16x8 neg136 = neg136_operand();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const bool xlive = r < m;  // lanes of rows past m keep zero activations
+  const uint16_t* xl = x + (size_t)min(r, m - 1) * K + 8 * kb;
+  const uint32_t loff = lane * 16, soff = r * 8;
+  const size_t tbase = (size_t)tile * Q;
 
+  auto issue = [&](int c, LongBuf& b) {
+#pragma unroll
+    for (int a = 0; a < kLongChunk; ++a) {
+      const int q = min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1);
+      const size_t blk = tbase + q;
+      b.w[a] = load16(nib + blk * 1024 + loff);
+      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+      if (xlive) {  // no write on the other side: the zeros stay
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b.x[a][j] = load16(xl + 32 * min(4 * q + j, G - 1));
+      }
+    }
+  };
+  f32x4 acc = zero4;
+  auto consume = [&](int c, const LongBuf& b) {
+#pragma unroll
+    for (int a = 0; a < kLongChunk; ++a) {
+      const bool real = c * kLongChunk + a < nq;  // uniform
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 xa = as_bf16x8(b.x[a][j]);
+        const f32x4 c0 = mfma16x16x32(xa, neg136, zero4);
+        const float sc = real ? scale_of(b.s[a], j) : 0.f;
+        w4_group(xa, c0, b.w[a][j], sc, acc);
+      }
+    }
+  };
   LongBuf A, B;
 #pragma unroll
   for (int a = 0; a < kLongChunk; ++a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) A.x[a][j] = B.x[a][j] = u32x4{0u, 0u, 0u, 0u};
-  auto issue = [&](int c, LongBuf& b) {
-#pragma unroll
-    for (int a = 0; a < kLongChunk; ++a) {
-      const int q = min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1);
-      const size_t blk = (size_t)tile * Q + q;
-      b.w[a] = load16(nib + blk * 1024 + lane * 16);
-      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + r * 8);
-      if (xlive) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b.x[a][j] = load16(xrow + min(128 * q + 32 * j + 8 * kb, K - 8));
-      }
-    }
-  };
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](int c, const LongBuf& b) {
-#pragma unroll
-    for (int a = 0; a < kLongChunk; ++a) {
-      const bool real = c * kLongChunk + a < nq;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float sc = real ? scale_of(b.s[a], j) : 0.f;
-        mfma_group(as_bf16x8(b.x[a][j]), b.w[a][j], sc, neg136, acc);
-      }
-    }
-  };
   issue(0, A);
   __builtin_amdgcn_sched_barrier(0);
   issue(1, B);
@@ -458,7 +533,8 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_long_kernel(
     issue(c + 3, B);
     __builtin_amdgcn_sched_barrier(0);
   }
-  gemv_group_store(red, acc, KS, TPW, g * TPW, true, n_tiles, m, N, y);
+  park(part, wave, acc);
+  flush_tiles(part, W, tile, 1, m, N, y);
 }
 
 // Expert-routed form. Block (pair slot ps, tile group): the expert of pair ps
@@ -544,6 +620,11 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_routed_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 
+static int env_int_w4(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
 size_t w4_packed_bytes(int N, int K) {
   const size_t nt = (size_t)(N + 15) / 16, q = (size_t)(K + 127) / 128;
   return nt * q * (1024 + 128);
@@ -573,33 +654,47 @@ hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K
   const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
   const uint8_t* nib = (const uint8_t*)packed;
   const uint8_t* scl = nib + (size_t)n_tiles * Q * 1024;
-  const int KS = gemv_ks(Q), tpw = kGemvWaves / KS;
-  const int n_groups = (n_tiles + tpw - 1) / tpw;
-  const int per = (Q + KS - 1) / KS;
   const uint16_t* xp = (const uint16_t*)x;
-  const dim3 block(kGemvThreads);
-  if (per <= 4) {
-    // up to two workgroups per CU: one tile group each; beyond that a
-    // persistent grid of one workgroup per CU walks runs of tile groups
-    const bool single = wgs_per_cu <= 0 && n_groups <= 2 * 256;
+  // short K: the fewest quads per wave (1, 2 or 4) whose slices cover K
+  // within the kernel's wave limit
+  int qpw = 0;
+  for (int c : {1, 2, 4})
+    if (qpw == 0 && (Q + c - 1) / c <= short_max_waves(c)) qpw = c;
+  const int forced = env_int_w4("SVE_GEMV_QPW", 0);
+  if (qpw > 0 && (forced == 1 || forced == 2 || forced == 4) &&
+      (Q + forced - 1) / forced <= short_max_waves(forced))
+    qpw = forced;
+  if (qpw > 0) {
+    const int W = (Q + qpw - 1) / qpw;
+    // one tile per workgroup while that fits one round of the chip (one
+    // workgroup per CU), else a grid of runs of at least two tiles
     const int per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
-    const dim3 grid(single ? n_groups : std::max(1, std::min(n_groups, 256 * per_cu)));
-#define SVE_SHORT(Q_, S_) \
-  hipLaunchKernelGGL((w4_gemv_short_kernel<Q_, S_>), grid, block, 0, st, xp, m, nib, scl, N, K, Q, n_tiles, y)
-    switch (per * 2 + (single ? 1 : 0)) {
-      case 2: SVE_SHORT(1, false); break;
-      case 3: SVE_SHORT(1, true); break;
-      case 4: SVE_SHORT(2, false); break;
-      case 5: SVE_SHORT(2, true); break;
-      case 6: SVE_SHORT(3, false); break;
-      case 7: SVE_SHORT(3, true); break;
-      case 8: SVE_SHORT(4, false); break;
-      default: SVE_SHORT(4, true); break;
+    const bool single = wgs_per_cu <= 0 && n_tiles <= 256;
+    const int grid = single ? n_tiles : std::max(1, std::min(n_tiles / 2, 256 * per_cu));
+    const int hoist_env = env_int_w4("SVE_GEMV_HOIST", -1);
+    const bool hoist = hoist_env >= 0 ? hoist_env != 0 : qpw == 1;
+#define SVE_SHORT(Q_, S_, H_)                                                                      \
+  hipLaunchKernelGGL((w4_gemv_short_kernel<Q_, S_, H_>), dim3(grid), dim3(64 * W), 0, st, xp, m, \
+                     nib, scl, N, K, Q, n_tiles, y)
+    switch (qpw * 4 + (single ? 2 : 0) + (hoist ? 1 : 0)) {
+      case 4: SVE_SHORT(1, false, false); break;
+      case 5: SVE_SHORT(1, false, true); break;
+      case 6: SVE_SHORT(1, true, false); break;
+      case 7: SVE_SHORT(1, true, true); break;
+      case 8: SVE_SHORT(2, false, false); break;
+      case 9: SVE_SHORT(2, false, true); break;
+      case 10: SVE_SHORT(2, true, false); break;
+      case 11: SVE_SHORT(2, true, true); break;
+      case 16: SVE_SHORT(4, false, false); break;
+      case 17: SVE_SHORT(4, false, true); break;
+      case 18: SVE_SHORT(4, true, false); break;
+      default: SVE_SHORT(4, true, true); break;  // 19
     }
 #undef SVE_SHORT
   } else {
-    hipLaunchKernelGGL(w4_gemv_long_kernel, dim3(n_groups), block, 0, st, xp, m, nib, scl, N, K, Q,
-                       n_tiles, y);
+    const int W = kLongMaxWaves;
+    hipLaunchKernelGGL(w4_gemv_long_kernel, dim3(n_tiles), dim3(64 * W), 0, st, xp, m, nib, scl, N,
+                       K, Q, n_tiles, y);
   }
   return hipGetLastError();
 }
