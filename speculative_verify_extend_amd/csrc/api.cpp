@@ -23,7 +23,8 @@ using namespace sve;
 
 namespace {
 
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 16;        // workspace: kMaxSplits x max_rows rows
+constexpr int kMaxDecodeSplits = 64;
 constexpr size_t kAlign = 256;
 thread_local std::string g_err;
 
@@ -134,12 +135,32 @@ int hip_fail(const sve_ctx* c, hipError_t e, const char* what) {
   } while (0)
 
 // Choose the path, row blocks and key splits of every piece of a call.
+//   decode: every piece has at most 64 packed rows (m*g) per KV head; a
+//           workgroup covers 32 packed rows and a key split of whole
+//           128-key rounds (4 waves x 32 keys)
+//   mfma:   longer suffixes, 128 packed rows per workgroup, 64-key tiles
+//   valu:   kept for comparison (SVE_MFMA_MIN_ROWS / SVE_ATTN_PATH select it)
+// Splits: as many as keep the grid near one round of workgroups, within 64
+// per piece and within the split workspace (16 x max_rows rows in total).
 void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
   const int g = p.g;
-  int max_m = 0;
-  for (int s = 0; s < p.nseg; ++s) max_m = std::max(max_m, p.seg[s].m);
-  const int mfma_min = env_int("SVE_MFMA_MIN_ROWS", 16);
-  path = (max_m >= mfma_min) ? kPathMfma : kPathValu;
+  int max_m = 0, max_r = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    max_m = std::max(max_m, p.seg[s].m);
+    max_r = std::max(max_r, p.seg[s].m * g);
+  }
+  const char* want = getenv("SVE_ATTN_PATH");
+  const int mfma_min = env_int("SVE_MFMA_MIN_ROWS", -1);
+  if (want && !strcmp(want, "valu"))
+    path = kPathValu;
+  else if (want && !strcmp(want, "mfma"))
+    path = kPathMfma;
+  else if (want && !strcmp(want, "decode"))
+    path = max_r <= 64 ? kPathDecode : kPathMfma;
+  else if (mfma_min > 0)
+    path = (max_m >= mfma_min) ? kPathMfma : kPathValu;
+  else
+    path = max_r <= 64 ? kPathDecode : kPathMfma;
   const int rpb = attn_rows_per_block(path);
   int base = 0;
   for (int s = 0; s < p.nseg; ++s) {
@@ -147,32 +168,58 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     base += p.Hkv * p.seg[s].row_blocks;
   }
   const int target = path == kPathValu ? 512 : 256;
+  const int unit = path == kPathDecode ? 128 : 64;  // split length granule (keys)
+  const int max_splits = path == kPathDecode ? kMaxDecodeSplits : kMaxSplits;
   const int forced = env_int("SVE_KV_SPLIT", 0);
+  const long long ws_cap = (long long)kMaxSplits * c->cfg.max_rows;  // workspace rows
+  long long ws_rows = 0;
   int blocks = 0, rows = 0;
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
-    const int keys = sg.P + sg.m;
-    // as many splits as keep the grid within one round of workgroups
+    const bool dec = path == kPathDecode;
+    // decode: the cached keys [0, P) are split, and one more split holds
+    // the new keys; other paths split all P + m keys uniformly
+    const int keys = dec ? sg.P : sg.P + sg.m;
+    // (whole rounds of workgroups: at most `target` workgroups in flight)
     int S = forced > 0 ? forced : target / std::max(base, 1);
-    S = std::max(1, std::min(S, kMaxSplits));
-    S = std::min(S, (keys + 63) / 64);
-    int sk = (keys + S - 1) / S;
-    sk = (sk + 63) / 64 * 64;
-    S = (keys + sk - 1) / sk;
+    S = std::max(1, std::min(S, max_splits));
+    // the pieces after this one keep at least one split row each
+    const long long room = ws_cap - ws_rows - (p.total_rows_hint - rows - sg.m);
+    S = (int)std::max(1LL, std::min<long long>(S, room / std::max(sg.m, 1)));
+    if (dec) S = std::max(S - 1, 1);  // cached splits
+    S = std::min(S, (keys + unit - 1) / unit);
+    int sk = 0;
+    if (keys > 0) {
+      sk = (keys + S - 1) / S;
+      sk = (sk + unit - 1) / unit * unit;
+      S = (keys + sk - 1) / sk;
+    } else {
+      S = 0;
+      sk = unit;
+    }
+    if (dec) ++S;  // + the new-key split
     sg.splits = S;
     sg.split_keys = sk;
+    sg.tail_split = dec ? 1 : 0;
     sg.block_begin = blocks;
     sg.row_begin = rows;
-    sg.ws_o = c->ws_o() + (size_t)rows * kMaxSplits * p.Hq * p.D;
-    sg.ws_ml = c->ws_ml() + (size_t)rows * kMaxSplits * p.Hq * 2;
+    sg.ws_o = c->ws_o() + (size_t)ws_rows * p.Hq * p.D;
+    sg.ws_ml = c->ws_ml() + (size_t)ws_rows * p.Hq * 2;
+    ws_rows += (long long)S * sg.m;
     blocks += p.Hkv * sg.row_blocks * S;
     rows += sg.m;
   }
   p.total_blocks = blocks;
   p.total_rows = rows;
+  if (path == kPathDecode) {
+    int max_sk = 0;
+    for (int s = 0; s < p.nseg; ++s) max_sk = std::max(max_sk, p.seg[s].split_keys);
+    p.dec_rt = max_r <= 16 ? 1 : 2;
+    p.dec_ns = max_sk >= 256 ? 2 : 1;
+  }
   if (log_on()) {
-    fprintf(stderr, "[sve] extend: path=%s pieces=%d blocks=%d", path == kPathMfma ? "mfma" : "valu",
-            p.nseg, blocks);
+    fprintf(stderr, "[sve] extend: path=%s pieces=%d blocks=%d",
+            path == kPathMfma ? "mfma" : path == kPathDecode ? "decode" : "valu", p.nseg, blocks);
     for (int s = 0; s < p.nseg; ++s)
       fprintf(stderr, " (P=%d m=%d splits=%d x %d keys)", p.seg[s].P, p.seg[s].m, p.seg[s].splits,
               p.seg[s].split_keys);
@@ -222,13 +269,17 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
     sg.m = ms[i];
     row += ms[i];
   }
+  p.total_rows_hint = total;
   int path = kPathMfma;
   plan_attention(c, p, path);
   hipEvent_t* ev = nullptr;
   if (c->timed_used < c->timed_max) ev = &c->tev[4 * (size_t)c->timed_used++];
   if (ev) SVE_HIP(c, hipEventRecord(ev[0], c->stream));
-  hipError_t e = launch_kv_append(p, c->stream);
-  if (e != hipSuccess) return hip_fail(c, e, "kv_append launch");
+  hipError_t e = hipSuccess;
+  if (path != kPathDecode) {  // the decode kernel appends its rows itself
+    e = launch_kv_append(p, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "kv_append launch");
+  }
   if (ev) SVE_HIP(c, hipEventRecord(ev[1], c->stream));
   e = launch_attn(p, path, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "extend_attn launch");

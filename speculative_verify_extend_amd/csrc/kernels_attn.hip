@@ -276,11 +276,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       grow |= mcand[rt] > mref[rt] + 8.f;
     }
     if (__ballot(grow) != 0) {
+      // only the rows that grew move their reference, so every row's
+      // arithmetic depends on that row alone
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const float mnew = fmaxf(mref[rt], mcand[rt]);
-        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mref[rt] - mnew);
-        mref[rt] = mnew;
+        const bool up = mcand[rt] > mref[rt] + 8.f;
+        const float alpha = up ? fast_exp2(mref[rt] - mcand[rt]) : 1.f;
+        mref[rt] = up ? mcand[rt] : mref[rt];
         lrun[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -392,6 +394,270 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         float* ml = sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 2;
         ml[0] = mref[rt];
         ml[1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode path: few rows per KV head (m*g <= 64 packed rows), as in a
+// speculative verify or a short question. Workgroup = (KV head, block of at
+// most 32 packed rows, key split). The cached keys [0, P) are cut into
+// splits of whole 128-key rounds; one more split holds exactly the call's
+// m new keys [P, P+m). The 4 waves of a workgroup take its 32-key steps in
+// turn (wave w: steps w, w+4, ...), NS steps per round, with every load of
+// a round issued at once straight from global memory into MFMA operand
+// registers: each workgroup has little work, so what keeps HBM busy is many
+// workgroups with all their loads in flight.
+//
+// The new-key split reads its keys from the call's inputs: K rows directly,
+// V rows transposed through LDS (zero past m). It also appends the new rows
+// to the cache (K rows copied, V columns written into Vt); no other
+// workgroup of the call reads those positions, so nothing waits for the
+// stores. The 32-key steps use the same key order as the MFMA path (lane
+// (row, kb) holds keys 8*kb .. 8*kb+7 of the step) and the four wave states
+// are merged in LDS in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kDecWaves = 4;
+constexpr int kDecRowsPerBlock = 32;
+constexpr int kDecMaxNew = 64;  // new keys per call on this path (m <= 64)
+
+template <int D, int RT, int NS>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams prm) {
+  constexpr int DC = D / 32, DT = D / 16, CPR = D / 8;
+  constexpr int XO = kDecWaves * RT * (DT + 1) * 64;  // f32x4 slots: wave states
+  static_assert(XO * 16 >= D * kDecMaxNew * 2, "new-row staging fits the merge area");
+  __shared__ f32x4 xo[XO];
+
+  const SegRef ref = find_seg(prm, xcd_linear(blockIdx.x, gridDim.x));
+  const AttnSeg& sg = prm.seg[ref.s];
+  const int S = sg.splits;
+  const int split = ref.local % S;
+  const int rest = ref.local / S;
+  const int rb = rest % sg.row_blocks, kvh = rest / sg.row_blocks;
+  const int g = prm.g, Hq = prm.Hq, Hkv = prm.Hkv, cap = prm.cap;
+  const int P = sg.P, m = sg.m, R = m * g;
+  const bool tail = split == S - 1;  // the new-key split (uniform)
+  const int k0 = tail ? P : split * sg.split_keys;
+  const int k1 = tail ? P + m : min(P, k0 + sg.split_keys);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, col = lane & 15;
+  uint16_t* Kg = const_cast<uint16_t*>(sg.K) + (size_t)kvh * cap * D;
+  uint16_t* Vg = const_cast<uint16_t*>(sg.Vt) + (size_t)kvh * D * cap;
+  const uint16_t* nkh = sg.nk + (size_t)kvh * D;  // new row r of this head: + r * Hkv * D
+  const uint16_t* nvh = sg.nv + (size_t)kvh * D;
+  const float cs = prm.c;
+
+  // query operands (B of S^T = K Q^T): lane (col, kb) holds packed row
+  // 32*rb + 16*rt + col, elements 32*dc + 8*kb .. +7
+  int lim[RT], qi[RT], qh[RT];
+  bool rvalid[RT];
+  bf16x8 qop[RT][DC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int pr = kDecRowsPerBlock * rb + 16 * rt + col;
+    rvalid[rt] = pr < R;
+    const int i = rvalid[rt] ? pr / g : 0;
+    qi[rt] = i;
+    qh[rt] = kvh * g + (rvalid[rt] ? pr % g : 0);
+    lim[rt] = min(P + i, k1 - 1);  // last visible key of this split
+    // padded rows read a live query row; their outputs are never stored
+    const uint16_t* qrow = sg.q + ((size_t)i * Hq + qh[rt]) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qop[rt][dc] = as_bf16x8(load16(qrow + 32 * dc + 8 * kb));
+  }
+
+  // new-key split: V rows transposed into LDS (Vs[d][r], r < 64, zero past
+  // m), then appended to the cache from there; K rows appended directly
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(xo);
+  if (tail) {
+    const int rows_used = (m + 31) / 32 * 32;  // the steps read up to here
+    for (int c = threadIdx.x; c < rows_used * CPR; c += 256) {
+      const int r = c / CPR, ch = c % CPR;
+      const size_t src = (size_t)min(r, m - 1) * Hkv * D + ch * 8;
+      const u32x4 v = load16(nvh + src);
+      const u32x4 kr = load16(nkh + src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vs[(ch * 8 + 2 * e) * kDecMaxNew + r] = r < m ? (uint16_t)(v[e] & 0xFFFFu) : 0;
+        Vs[(ch * 8 + 2 * e + 1) * kDecMaxNew + r] = r < m ? (uint16_t)(v[e] >> 16) : 0;
+      }
+      if (r < m) store16(Kg + (size_t)(P + r) * D + ch * 8, kr);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < D * m; c += 256) {
+      const int d = c / m, r = c % m;
+      Vg[(size_t)d * cap + P + r] = Vs[d * kDecMaxNew + r];
+    }
+  }
+
+  f32x4 O[RT][DT];
+  float mref[RT], lrun[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    mref[rt] = -INFINITY;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nsteps = (k1 - k0 + 31) / 32;
+  for (int u0 = 0; wave + kDecWaves * u0 < nsteps; u0 += NS) {
+    bf16x8 kop[NS][2][DC], vop[NS][DT];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      // steps past the range re-read the range's first step (discarded)
+      const int st = wave + kDecWaves * (u0 + u);
+      const int sst = st < nsteps ? st : 0;
+      const int kbase = k0 + 32 * sst;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int key = kbase + 8 * (col >> 2) + 4 * sub + (col & 3);
+        // cached keys read the store (positions up to the next 32-key
+        // boundary exist and are masked); new keys read the call's rows
+        const uint16_t* krow = tail ? nkh + (size_t)min(key - P, m - 1) * Hkv * D
+                                    : Kg + (size_t)key * D;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          kop[u][sub][dc] = as_bf16x8(load16(krow + 32 * dc + 8 * kb));
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + col;
+        vop[u][dt] = tail ? as_bf16x8(*reinterpret_cast<const u32x4*>(
+                                Vs + d * kDecMaxNew + 32 * sst + 8 * kb))
+                          : as_bf16x8(load16(Vg + (size_t)d * cap + kbase + 8 * kb));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int st = wave + kDecWaves * (u0 + u);
+      if (st >= nsteps) break;  // uniform
+      const int kbase = k0 + 32 * st;
+      f32x4 Sc[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          Sc[rt][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc)
+            Sc[rt][sub] = mfma16x16x32(kop[u][sub][dc], qop[rt][dc], Sc[rt][sub]);
+        }
+      bool grow = false;
+      float mcand[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + 8 * kb + 4 * sub + i;
+            const float v = (key <= lim[rt]) ? Sc[rt][sub][i] : -INFINITY;
+            Sc[rt][sub][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = max4_rows(mx);
+        mcand[rt] = mx * cs;
+        grow |= mcand[rt] > mref[rt] + 8.f;
+      }
+      if (__ballot(grow) != 0) {
+        // only the rows that grew move their reference, so every row's
+        // arithmetic depends on that row alone
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bool up = mcand[rt] > mref[rt] + 8.f;
+          const float alpha = up ? fast_exp2(mref[rt] - mcand[rt]) : 1.f;
+          mref[rt] = up ? mcand[rt] : mref[rt];
+          lrun[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[rt][dt][i] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float muse = (mref[rt] == -INFINITY) ? 0.f : mref[rt];
+        float psum = lrun[rt];
+        u32x4 pk;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = fast_exp2(fmaf(Sc[rt][sub][i], cs, -muse));
+            const float p1 = fast_exp2(fmaf(Sc[rt][sub][i + 1], cs, -muse));
+            const uint32_t w = pack_bf16x2(p0, p1);
+            pk[2 * sub + (i >> 1)] = w;
+            psum = dot2_bf16(w, 0x3F803F80u, psum);  // + both bf16 values exactly
+          }
+        lrun[rt] = psum;
+        const bf16x8 pb = as_bf16x8(pk);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[rt][dt] = mfma16x16x32(vop[u][dt], pb, O[rt][dt]);
+      }
+    }
+  }
+
+  // park the wave states (the staging area is reused: wait for every wave),
+  // then merge them in wave order: wave w finishes d tiles w, w+4, ...
+  if (tail) __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = lrun[rt];
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    const int base = (wave * RT + rt) * (DT + 1);
+    xo[base * 64 + lane] = f32x4{mref[rt], l, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) xo[(base + 1 + dt) * 64 + lane] = O[rt][dt];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float M = -INFINITY;
+    float mw[kDecWaves], lw[kDecWaves];
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const f32x4 ml = xo[((w * RT + rt) * (DT + 1)) * 64 + lane];
+      mw[w] = ml[0];
+      lw[w] = ml[1];
+      M = fmaxf(M, ml[0]);
+    }
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float sw[kDecWaves], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      sw[w] = fast_exp2(mw[w] - Mu);
+      L += sw[w] * lw[w];
+    }
+    const bool store = rvalid[rt] && k0 <= lim[rt];
+    const size_t orow = ((size_t)qi[rt] * Hq + qh[rt]) * D;
+    for (int dt = wave; dt < DT; dt += kDecWaves) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const f32x4 ow = xo[((w * RT + rt) * (DT + 1) + 1 + dt) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] += sw[w] * ow[i];
+      }
+      if (!store) continue;
+      if (S == 1) {
+        const float inv = 1.f / L;
+        u32x2 w2;
+        w2[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+        w2[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+        *reinterpret_cast<u32x2*>(sg.out + orow + 16 * dt + 4 * kb) = w2;
+      } else {
+        *reinterpret_cast<f32x4*>(sg.ws_o + (size_t)split * m * Hq * D + orow + 16 * dt + 4 * kb) =
+            o;
+        if (dt == 0 && kb == 0) {
+          float* ml = sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 2;
+          ml[0] = M;
+          ml[1] = L;
+        }
       }
     }
   }
@@ -589,47 +855,83 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
 // splits that contain at least one key the row can see, in split order.
 // grid over rows (i, h) of all pieces; 4 columns per thread.
 // ---------------------------------------------------------------------------
-template <int D>
+// One wave per (row, q head), four per workgroup. Lane (chunk, part): D/4
+// chunks of 4 columns times 256/D parts; part t merges splits t, t+P,
+// t+2P, ... (P = 256/D), loading BATCH of them per round, and the parts are
+// then merged in part order through lane shuffles. Every (row, head) is
+// merged in the same fixed order whatever the launch shape.
+template <int D, int BATCH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
-  constexpr int TPR = D / 4;  // threads per (i, h) row
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = t / TPR;
-  const int c4 = (int)(t % TPR) * 4;
-  if (row >= (long long)p.total_rows * p.Hq) return;
-  const int grow = (int)(row / p.Hq), h = (int)(row % p.Hq);
+  constexpr int CH = D / 4, PARTS = 64 / CH;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (grow, h): one per wave
+  if (row >= p.total_rows * p.Hq) return;
+  const int grow = row / p.Hq, h = row % p.Hq;
   int s = 0;
 #pragma unroll
   for (int j = 1; j < kMaxSeg; ++j)
     if (j < p.nseg && grow >= p.seg[j].row_begin) s = j;
   const AttnSeg& sg = p.seg[s];
   if (sg.splits == 1) return;
+  const int lane = threadIdx.x & 63;
+  const int c4 = (lane % CH) * 4, part = lane / CH;
   const int i = grow - sg.row_begin;
-  const int nvalid = min(sg.splits, (sg.P + i) / sg.split_keys + 1);
-  // all loads first (one round trip), then the fixed-order merge
-  float2 ml[16];
-  f32x4 o[16];
-#pragma unroll
-  for (int sp = 0; sp < 16; ++sp) {
-    const int q = min(sp, nvalid - 1);
-    const size_t r = ((size_t)q * sg.m + i) * p.Hq + h;
-    ml[sp] = *reinterpret_cast<const float2*>(sg.ws_ml + r * 2);
-    o[sp] = *reinterpret_cast<const f32x4*>(sg.ws_o + r * D + c4);
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int sp = 0; sp < 16; ++sp)
-    if (sp < nvalid) M = fmaxf(M, ml[sp].x);
+  // uniform splits: those starting at or before the row's last key; the
+  // decode layout (cached splits + one new-key split): all of them
+  const int nvalid =
+      sg.tail_split ? sg.splits : min(sg.splits, (sg.P + i) / sg.split_keys + 1);
+  const float* mlp = sg.ws_ml + ((size_t)i * p.Hq + h) * 2;
+  const float* op = sg.ws_o + ((size_t)i * p.Hq + h) * D + c4;
+  const size_t ml_stride = (size_t)sg.m * p.Hq * 2, o_stride = (size_t)sg.m * p.Hq * D;
+  float M = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
+  for (int b0 = 0; b0 * PARTS < nvalid; b0 += BATCH) {
+    float2 ml[BATCH];
+    f32x4 o[BATCH];
 #pragma unroll
-  for (int sp = 0; sp < 16; ++sp) {
-    if (sp < nvalid) {
-      const float sc = fast_exp2(ml[sp].x - M);
-      l += sc * ml[sp].y;
+    for (int u = 0; u < BATCH; ++u) {
+      const size_t q = (size_t)min((b0 + u) * PARTS + part, nvalid - 1);
+      ml[u] = *reinterpret_cast<const float2*>(mlp + q * ml_stride);
+      o[u] = *reinterpret_cast<const f32x4*>(op + q * o_stride);
+    }
+    float Mb = M;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += sc * o[sp][e];
+    for (int u = 0; u < BATCH; ++u)
+      if ((b0 + u) * PARTS + part < nvalid) Mb = fmaxf(Mb, ml[u].x);
+    const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
+    l *= r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= r;
+    M = Mb;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if ((b0 + u) * PARTS + part < nvalid) {
+        const float sc = fast_exp2(ml[u].x - M);
+        l += sc * ml[u].y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += sc * o[u][e];
+      }
     }
   }
+  // merge the parts in order: part 0 absorbs parts 1 .. PARTS-1 (always
+  // reading the other parts' own states, never a partly merged one)
+  const float Mp = M, lp = l;
+  const f32x4 ap = acc;
+#pragma unroll
+  for (int t = 1; t < PARTS; ++t) {
+    const float Mt = __shfl(Mp, (lane % CH) + t * CH, 64);
+    const float lt = __shfl(lp, (lane % CH) + t * CH, 64);
+    f32x4 at;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) at[e] = __shfl(ap[e], (lane % CH) + t * CH, 64);
+    const float Mn = fmaxf(M, Mt);
+    const float Mu = (Mn == -INFINITY) ? 0.f : Mn;
+    const float r0 = fast_exp2(M - Mu), r1 = fast_exp2(Mt - Mu);
+    l = l * r0 + lt * r1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * r0 + at[e] * r1;
+    M = Mn;
+  }
+  if (part != 0) return;
   const float inv = 1.f / l;
   u32x2 w;
   w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
@@ -654,7 +956,9 @@ __global__ __launch_bounds__(256) void kv_read_kernel(const uint16_t* K, const u
 // host launchers
 // ---------------------------------------------------------------------------
 
-int attn_rows_per_block(int path) { return path == kPathValu ? kValuRows : 64 * 2; }
+int attn_rows_per_block(int path) {
+  return path == kPathValu ? kValuRows : path == kPathDecode ? kDecRowsPerBlock : 64 * 2;
+}
 
 hipError_t launch_kv_append(const AttnParams& p, hipStream_t st) {
   int maxm = 0;
@@ -668,10 +972,26 @@ hipError_t launch_kv_append(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D>
+static void launch_decode(const AttnParams& p, int rt, int ns, hipStream_t st) {
+  const dim3 grid(p.total_blocks), block(256);
+  switch (rt * 2 + ns) {
+    case 3: hipLaunchKernelGGL((attn_decode_kernel<D, 1, 1>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 1, 2>), grid, block, 0, st, p); break;
+    case 5: hipLaunchKernelGGL((attn_decode_kernel<D, 2, 1>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_decode_kernel<D, 2, 2>), grid, block, 0, st, p); break;
+  }
+}
+
 hipError_t launch_attn(const AttnParams& p, int path, hipStream_t st) {
   if (p.total_blocks == 0) return hipSuccess;
   const dim3 grid(p.total_blocks), block(256);
-  if (path == kPathValu) {
+  if (path == kPathDecode) {
+    if (p.D == 128)
+      launch_decode<128>(p, p.dec_rt, p.dec_ns, st);
+    else
+      launch_decode<64>(p, p.dec_rt, p.dec_ns, st);
+  } else if (path == kPathValu) {
     if (p.D == 128)
       hipLaunchKernelGGL(attn_valu_kernel<128>, grid, block, 0, st, p);
     else
@@ -689,12 +1009,22 @@ hipError_t launch_attn_combine(const AttnParams& p, hipStream_t st) {
   bool any = false;
   for (int s = 0; s < p.nseg; ++s) any |= p.seg[s].splits > 1 && p.seg[s].m > 0;
   if (!any) return hipSuccess;
-  const long long threads = (long long)p.total_rows * p.Hq * (p.D / 4);
-  const int blocks = (int)((threads + 255) / 256);
-  if (p.D == 128)
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(blocks), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(blocks), dim3(256), 0, st, p);
+  int max_s = 0;
+  for (int s = 0; s < p.nseg; ++s) max_s = p.seg[s].splits > max_s ? p.seg[s].splits : max_s;
+  const int blocks = (p.total_rows * p.Hq + 3) / 4;
+  // splits loaded per part and round: few splits -> short rounds
+  const bool wide = max_s > (p.D == 128 ? 8 : 16);
+  if (p.D == 128) {
+    if (wide)
+      hipLaunchKernelGGL((attn_combine_kernel<128, 16>), dim3(blocks), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<128, 4>), dim3(blocks), dim3(256), 0, st, p);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((attn_combine_kernel<64, 16>), dim3(blocks), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<64, 4>), dim3(blocks), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

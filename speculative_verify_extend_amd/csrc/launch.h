@@ -29,11 +29,12 @@ struct AttnSeg {
   const uint16_t* nk;  // new rows [m][Hkv][D]
   const uint16_t* nv;
   uint16_t* out;       // [m][Hq][D]
-  float* ws_o;         // [splits][m][Hq][D]
+  float* ws_o;         // [splits][m][Hq][D] (this piece's part of the workspace)
   float* ws_ml;        // [splits][m][Hq][2]
   int P, m;
   int row_blocks;      // per KV head
   int splits, split_keys;
+  int tail_split;      // decode layout: splits-1 cached splits of split_keys, then [P, P+m)
   int block_begin;     // first linear workgroup of this piece
   int row_begin;       // first output row of this piece in a combined launch
 };
@@ -45,9 +46,11 @@ struct AttnParams {
   int total_blocks;
   int total_rows;      // sum of m over pieces
   float c;             // log2(e) / sqrt(D)
+  int dec_rt, dec_ns;  // decode path: 16-row tiles per block (1, 2), steps per round (1, 2)
+  int total_rows_hint; // rows of the whole call (planning only)
 };
 
-enum AttnPath { kPathValu = 0, kPathMfma = 1 };
+enum AttnPath { kPathValu = 0, kPathMfma = 1, kPathDecode = 2 };
 
 // rows of packed (query row, head-in-group) per workgroup for each path
 int attn_rows_per_block(int path);

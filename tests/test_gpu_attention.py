@@ -16,7 +16,9 @@ from tests.gpu_helpers import (announce, dev_bf16, env, host_bits, host_f64_of_b
 pytestmark = pytest.mark.gpu
 ATTN_TOL = 1e-2  # max-abs against the fp64 oracle
 
-PATHS = {"valu": dict(SVE_MFMA_MIN_ROWS=100000), "mfma": dict(SVE_MFMA_MIN_ROWS=1)}
+PATHS = {"valu": dict(SVE_MFMA_MIN_ROWS=100000), "mfma": dict(SVE_MFMA_MIN_ROWS=1),
+         "decode": dict(SVE_ATTN_PATH="decode")}  # decode: pieces of <= 64 packed rows
+ALL_PATHS = ["valu", "mfma", "decode"]
 
 
 @pytest.fixture(autouse=True)
@@ -60,7 +62,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "h%d-%d-d%d-P%d-m%d" % c)
 def test_extend_matches_oracle(case, path):
     hq, hkv, d, prefix, m = case
@@ -69,12 +71,61 @@ def test_extend_matches_oracle(case, path):
     assert np.abs(got - want).max() <= ATTN_TOL
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("split", [1, 2, 5, 16])
 def test_key_splits(path, split):
     announce(f"splits={split} path={path}")
     got, want, _, _ = _run_case(8, 2, 128, 700, 21, path, seed=3, split=split)
     assert np.abs(got - want).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("split", [1, 3, 12, 40, 64])
+@pytest.mark.parametrize("m", [1, 6])
+def test_decode_key_splits(m, split):
+    """Decode path (verify-sized pieces) with forced key splits, up to the
+    path's 64-split limit, including splits that hold only cached rows."""
+    announce(f"decode splits={split} m={m}")
+    got, want, _, _ = _run_case(32, 8, 128, 1500, m, "decode", seed=12, split=split)
+    assert np.abs(got - want).max() <= ATTN_TOL
+
+
+def test_decode_batched_matches_single_slot_calls():
+    """Four verify-sized pieces (m = 1, 3, 8, 5 on 9B-like heads) in one
+    decode launch equal four separate calls and the oracle."""
+    hq, hkv, d = 32, 8, 128
+    Ps, ms = [700, 1030, 64, 1900], [1, 3, 8, 5]
+    sts = [sve.KVSlots(4, 1, hq, hkv, d, 2048, 2048) for _ in range(2)]
+    cases = [synth.attention_case(50 + i, hq, hkv, d, Ps[i], ms[i]) for i in range(4)]
+    announce("decode batched")
+    for st in sts:
+        for i in range(4):
+            toks = np.concatenate([[i + 1], np.arange(Ps[i] + ms[i] - 1)]).astype(np.int32)
+            slot, r = st.kv_slot_select(toks)
+            assert (slot, r) == (i, 0)
+            st.extend_attn(slot, 0, dev_bf16(cases[i]["q_prefix"]),
+                           dev_bf16(cases[i]["k_prefix"]), dev_bf16(cases[i]["v_prefix"]))
+    q = dev_bf16(np.concatenate([c["q"] for c in cases]))
+    k = dev_bf16(np.concatenate([c["k"] for c in cases]))
+    v = dev_bf16(np.concatenate([c["v"] for c in cases]))
+    with env(**PATHS["decode"]):
+        out_b = host_f64_of_bf16(sts[0].extend_attn_batched([0, 1, 2, 3], ms, 0, q, k, v))
+    row = 0
+    for i in range(4):
+        c = cases[i]
+        with env(**PATHS["decode"]):
+            single = host_f64_of_bf16(sts[1].extend_attn(i, 0, dev_bf16(c["q"]), dev_bf16(c["k"]),
+                                                         dev_bf16(c["v"])))
+        want = extend_attention(c["q"], np.concatenate([c["k_prefix"], c["k"]]),
+                                np.concatenate([c["v_prefix"], c["v"]]), Ps[i])
+        part = out_b[row:row + ms[i]]
+        assert np.abs(part - want).max() <= ATTN_TOL
+        assert np.abs(part - single).max() <= ATTN_TOL
+        row += ms[i]
+    for st in sts:
+        for i in range(4):
+            kk, vv = st.kv_read(i, 0, Ps[i], ms[i])
+            assert np.array_equal(host_bits(kk), cases[i]["k"])
+            assert np.array_equal(host_bits(vv), cases[i]["v"])
 
 
 def test_turn9_full_size():
@@ -85,7 +136,7 @@ def test_turn9_full_size():
     assert np.abs(got - want).max() <= ATTN_TOL
 
 
-@pytest.mark.parametrize("m", [1, 4, 8])
+@pytest.mark.parametrize("m", list(range(1, 9)))
 def test_verify_full_size(m):
     """Speculative verify: 2048 cached + m rows, 32 q / 8 KV heads, D 128, on
     the default path for that m."""
@@ -100,7 +151,7 @@ def test_verify_full_size(m):
     assert np.abs(host_f64_of_bf16(out) - want).max() <= ATTN_TOL
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("path", ALL_PATHS)
 def test_extend_equals_tail_of_full_prefill(path):
     """Extend over a cached prefix == the last rows of a from-scratch prefill
     of the whole sequence, both on the GPU."""
@@ -120,7 +171,9 @@ def test_extend_equals_tail_of_full_prefill(path):
 def test_token_by_token_equals_one_pass_bitwise(path):
     """Within one kernel path and without key splits, m one-row calls give the
     same bits as one m-row call: each row's arithmetic depends only on its own
-    query and the keys it sees, in absolute-position tile order."""
+    query and the keys it sees, in absolute-position tile order. (The decode
+    path splits at the cached length, which moves with each call; it is
+    checked to tolerance below.)"""
     hq, hkv, d, P, m = 8, 2, 128, 90, 12
     c = synth.attention_case(7, hq, hkv, d, P, m)
     announce(f"token-by-token path={path}")
@@ -142,20 +195,53 @@ def test_token_by_token_equals_one_pass_bitwise(path):
     assert np.array_equal(outs[0], outs[1])
 
 
+def test_decode_token_by_token_matches_one_pass():
+    """Decode path: m one-row calls (each splitting at its own cached length)
+    agree with one m-row call and with the oracle within tolerance."""
+    hq, hkv, d, P, m = 32, 8, 128, 300, 8
+    c = synth.attention_case(13, hq, hkv, d, P, m)
+    announce("decode token-by-token")
+    outs = []
+    for mode in ("one", "many"):
+        st = _store(hq, hkv, d, P + m + 64, P + m)
+        st.kv_slot_select(np.arange(P + m, dtype=np.int32))
+        st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]),
+                       dev_bf16(c["v_prefix"]))
+        with env(**PATHS["decode"]):
+            if mode == "one":
+                outs.append(host_f64_of_bf16(st.extend_attn(0, 0, dev_bf16(c["q"]),
+                                                            dev_bf16(c["k"]), dev_bf16(c["v"]))))
+            else:
+                outs.append(np.concatenate([
+                    host_f64_of_bf16(st.extend_attn(0, 0, dev_bf16(c["q"][i:i + 1]),
+                                                    dev_bf16(c["k"][i:i + 1]),
+                                                    dev_bf16(c["v"][i:i + 1])))
+                    for i in range(m)]))
+    want = extend_attention(c["q"], np.concatenate([c["k_prefix"], c["k"]]),
+                            np.concatenate([c["v_prefix"], c["v"]]), P)
+    assert np.abs(outs[0] - outs[1]).max() <= 2 * ATTN_TOL
+    for o in outs:
+        assert np.abs(o - want).max() <= ATTN_TOL
+
+
 def test_paths_agree_within_tolerance():
     """The VALU and MFMA paths differ only by rounding (bf16 probabilities in
     the MFMA value product); both stay within the oracle tolerance."""
     announce("paths agree")
     a, want, _, _ = _run_case(16, 4, 128, 400, 9, "valu", seed=8)
     b, _, _, _ = _run_case(16, 4, 128, 400, 9, "mfma", seed=8)
-    assert np.abs(a - b).max() <= 2 * ATTN_TOL
-    assert np.abs(a - want).max() <= ATTN_TOL and np.abs(b - want).max() <= ATTN_TOL
+    c, _, _, _ = _run_case(16, 4, 128, 400, 9, "decode", seed=8)
+    for x in (b, c):
+        assert np.abs(a - x).max() <= 2 * ATTN_TOL
+    for x in (a, b, c):
+        assert np.abs(x - want).max() <= ATTN_TOL
 
 
-def test_cached_rows_are_the_appended_rows():
+@pytest.mark.parametrize("path", ALL_PATHS)
+def test_cached_rows_are_the_appended_rows(path):
     hq, hkv, d, P, m = 4, 2, 64, 70, 9
-    announce("kv read")
-    _, _, c, st = _run_case(hq, hkv, d, P, m, "mfma", seed=9)
+    announce(f"kv read path={path}")
+    _, _, c, st = _run_case(hq, hkv, d, P, m, path, seed=9)
     k, v = st.kv_read(0, 0, 0, P + m)
     assert np.array_equal(host_bits(k), np.concatenate([c["k_prefix"], c["k"]]))
     assert np.array_equal(host_bits(v), np.concatenate([c["v_prefix"], c["v"]]))
