@@ -458,10 +458,16 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kerne
 
 constexpr int kLongChunk = 2;  // quads per pipeline step
 
+constexpr int kLongStepK = 128 * kLongChunk;  // k per pipeline step
+
+// Weights and scales of one step, plus the step's activations in compact
+// form: m rows x kLongStepK elements, 16 bytes per lane and load (at most 8
+// loads for m <= 16), instead of the MFMA operand layout (eight loads per
+// step whatever m is).
 struct LongBuf {
   u32x4 w[kLongChunk];
   u32x2 s[kLongChunk];
-  u32x4 x[kLongChunk][4];
+  u32x4 xc[8];
 };
 
 constexpr int kLongMaxWaves = 8;
@@ -470,44 +476,57 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
     const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
   __shared__ f32x4 part[kGemvMaxWaves * 64];
+  // per wave: one step's activations, [row][kLongStepK] bf16, rewritten
+  // every step (LDS operations of a wave complete in order)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kLongMaxWaves][16 * kLongStepK];
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kb = lane >> 4, r = lane & 15;
-  const int G = K >> 5;
   const int tile = blockIdx.x;
   const int per = (Q + W - 1) / W;
   const int q0 = wave * per;
   const int nq = max(0, min(per, Q - q0));
   const int nchunks = (per + kLongChunk - 1) / kLongChunk;  // same for every wave
+  const int nu = (m + 1) / 2;  // compact activation loads per step (2 rows each)
   const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  const bool xlive = r < m;  // lanes of rows past m keep zero activations
-  const uint16_t* xl = x + (size_t)min(r, m - 1) * K + 8 * kb;
   const uint32_t loff = lane * 16, soff = r * 8;
   const size_t tbase = (size_t)tile * Q;
+  const int xr = min(r, m - 1);  // operand row (rows past m repeat row m-1; never stored)
+  uint16_t* xw = xs[wave];
 
+  auto quad_of = [&](int c, int a) { return min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1); };
   auto issue = [&](int c, LongBuf& b) {
 #pragma unroll
     for (int a = 0; a < kLongChunk; ++a) {
-      const int q = min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1);
-      const size_t blk = tbase + q;
+      const size_t blk = tbase + quad_of(c, a);
       b.w[a] = load16(nib + blk * 1024 + loff);
       b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
-      if (xlive) {  // no write on the other side: the zeros stay
+    }
+    // compact activations: lane slot e = lane + 64u holds row e / 32,
+    // elements 8 * (e % 32) .. +7 of the step (quad (e % 32) / 16)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b.x[a][j] = load16(xl + 32 * min(4 * q + j, G - 1));
+    for (int u = 0; u < 8; ++u) {
+      if (u < nu) {  // uniform
+        const int e = lane + 64 * u, rr = e >> 5, kc = e & 31;
+        const int k = min(128 * quad_of(c, kc >> 4) + 8 * (kc & 15), K - 8);
+        if (rr < m) b.xc[u] = load16(x + (size_t)rr * K + k);  // no write on the other side
       }
     }
   };
   f32x4 acc = zero4;
   auto consume = [&](int c, const LongBuf& b) {
 #pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < nu) store16(xw + 8 * (lane + 64 * u), b.xc[u]);
+#pragma unroll
     for (int a = 0; a < kLongChunk; ++a) {
       const bool real = c * kLongChunk + a < nq;  // uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 xa = as_bf16x8(b.x[a][j]);
+        const bf16x8 xa =
+            as_bf16x8(load16(xw + xr * kLongStepK + 128 * a + 32 * j + 8 * kb));
         const f32x4 c0 = mfma16x16x32(xa, neg136, zero4);
         const float sc = real ? scale_of(b.s[a], j) : 0.f;
         w4_group(xa, c0, b.w[a][j], sc, acc);
@@ -515,10 +534,6 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     }
   };
   LongBuf A, B;
-#pragma unroll
-  for (int a = 0; a < kLongChunk; ++a)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) A.x[a][j] = B.x[a][j] = u32x4{0u, 0u, 0u, 0u};
   issue(0, A);
   __builtin_amdgcn_sched_barrier(0);
   issue(1, B);
