@@ -404,10 +404,24 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kerne
     for (int a = 0; a < QPW; ++a) {
       const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
       b.w[a] = load16(nib + blk * 1024 + loff);
-      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+      if constexpr (QPW != 2) b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+    }
+    if constexpr (QPW == 2) {
+      // one scale load for both quads: lanes kb < 2 fetch quad 0's row,
+      // lanes kb >= 2 quad 1's (spread to every lane when consumed)
+      const size_t blk = (size_t)t * Q + min(q0 + (kb >> 1), Q - 1);
+      b.s[0] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
     }
   };
-  auto consume = [&](const TileBuf<QPW>& b) {
+  auto consume = [&](TileBuf<QPW> b) {
+    if constexpr (QPW == 2) {
+      const u32x2 own = b.s[0];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        b.s[0][e] = __shfl(own[e], r, 64);       // a lane with kb = 0
+        b.s[1][e] = __shfl(own[e], r + 32, 64);  // a lane with kb = 2
+      }
+    }
     f32x4 acc = zero4;
 #pragma unroll
     for (int a = 0; a < QPW; ++a)
@@ -497,13 +511,15 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
   uint16_t* xw = xs[wave];
 
   auto quad_of = [&](int c, int a) { return min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1); };
+  static_assert(kLongChunk == 2, "one scale load serves the two quads of a step");
   auto issue = [&](int c, LongBuf& b) {
 #pragma unroll
     for (int a = 0; a < kLongChunk; ++a) {
       const size_t blk = tbase + quad_of(c, a);
       b.w[a] = load16(nib + blk * 1024 + loff);
-      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
     }
+    // lanes kb < 2 fetch quad 0's scale row, lanes kb >= 2 quad 1's
+    b.s[0] = *reinterpret_cast<const u32x2*>(scl + (tbase + quad_of(c, kb >> 1)) * 128 + soff);
     // compact activations: lane slot e = lane + 64u holds row e / 32,
     // elements 8 * (e % 32) .. +7 of the step (quad (e % 32) / 16)
 #pragma unroll
@@ -516,7 +532,13 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     }
   };
   f32x4 acc = zero4;
-  auto consume = [&](int c, const LongBuf& b) {
+  auto consume = [&](int c, LongBuf b) {
+    const u32x2 own = b.s[0];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      b.s[0][e] = __shfl(own[e], r, 64);       // a lane with kb = 0
+      b.s[1][e] = __shfl(own[e], r + 32, 64);  // a lane with kb = 2
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (u < nu) store16(xw + 8 * (lane + 64 * u), b.xc[u]);
