@@ -653,6 +653,137 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_routed_kernel(
   }
 }
 
+// Expert-routed form on the dense short kernel's pipeline (K of at most 32
+// quads). Workgroup (run of row tiles, pair slot ps): the expert of pair ps
+// is handled by the first pair slot that names it; that workgroup gathers
+// every pair routed to the expert (16 per pass) as the rows of the MFMA
+// tile, keeps their activations (and C0) in registers, one k slice per
+// wave, and walks its run of the expert's row tiles double buffered. Each
+// distinct expert's weights therefore stream through the chip once, spread
+// over many workgroups.
+constexpr int kRoutedRun = 2;        // row tiles per workgroup
+constexpr int kRoutedMaxPairs = 256;  // m * topk (16 x 16)
+
+template <int QPW>
+__global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_short_kernel(
+    const uint16_t* __restrict__ x, int x_per_slot, int m, const int32_t* __restrict__ ids,
+    int topk, const uint8_t* __restrict__ packed_all, size_t expert_bytes, size_t scale_off,
+    int E, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
+  __shared__ f32x4 part[kGemvMaxWaves * kRoutedRun * 64];
+  __shared__ int sid[kRoutedMaxPairs];  // the routing table, read once
+  __shared__ int rows[16];
+  __shared__ int s_next;
+  const int ps = blockIdx.y;
+  const int npairs = m * topk;
+  for (int t = threadIdx.x; t < npairs; t += blockDim.x) sid[t] = ids[t];
+  __syncthreads();
+  const int e = sid[ps];
+  bool earlier = false;
+  for (int t = threadIdx.x; t < ps; t += blockDim.x) earlier |= sid[t] == e;
+  if (__syncthreads_or(earlier)) return;  // an earlier pair slot owns this expert
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, r = lane & 15;
+  const int G = K >> 5;
+  const int t0 = blockIdx.x * kRoutedRun, t1 = min(n_tiles, t0 + kRoutedRun);
+  if (t0 >= t1) return;
+  const int nt = t1 - t0;
+  const bool valid = (e >= 0 && e < E);
+  const uint8_t* nib = packed_all + (valid ? (size_t)e * expert_bytes : 0);
+  const uint8_t* scl = nib + scale_off;
+  const int q0 = wave * QPW;
+  const int nq = max(0, min(QPW, Q - q0));
+  const bf16x8 neg136 = neg136_operand();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t loff = lane * 16, soff = r * 8;
+
+  int start = ps;  // pairs with this expert all sit at or after ps
+  while (true) {
+    __syncthreads();
+    if (wave == 0) {
+      // the first 16 pairs at or after `start` routed to e, in pair order
+      // (ballot compaction), and the one after them
+      int c = 0, nxt = npairs;
+      for (int c0 = 0; c0 < npairs; c0 += 64) {
+        const int p = c0 + lane;
+        const bool hit = p >= start && p < npairs && sid[p] == e;
+        const unsigned long long mask = __ballot(hit);
+        const int pos = c + __popcll(mask & ((1ull << lane) - 1));
+        if (hit && pos < 16) rows[pos] = p;
+        if (hit && pos == 16) nxt = p;
+        c += __popcll(mask);
+      }
+      if (lane >= c && lane < 16) rows[lane] = -1;
+      nxt = __reduce_min_sync(~0ull, nxt);
+      if (lane == 0) s_next = nxt;
+    }
+    __syncthreads();
+    const int cnt = min(16, __popcll(__ballot(lane < 16 && rows[lane] >= 0)));
+    const int next = s_next;
+    if (!valid) {
+      // out-of-range expert id: its outputs are NaN
+      for (int c = threadIdx.x; c < cnt * nt * 16; c += blockDim.x) {
+        const int j = c / (nt * 16), n = 16 * t0 + c % (nt * 16);
+        if (n < N) y[(size_t)rows[j] * N + n] = __builtin_nanf("");
+      }
+    } else {
+      // activations of the gathered pairs (rows past cnt repeat the last
+      // pair and are never stored); quads past K meet zero activations
+      const int pr = rows[min(r, cnt - 1)];
+      const uint16_t* xrow =
+          (x_per_slot ? x + (size_t)pr * K : x + (size_t)(pr / topk) * K) + 8 * kb;
+      bf16x8 xa[QPW][4];
+#pragma unroll
+      for (int a = 0; a < QPW; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xa[a][j] = a < nq ? as_bf16x8(load16(xrow + 32 * min(4 * (q0 + a) + j, G - 1)))
+                            : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      auto issue = [&](int t, TileBuf<QPW>& b) {
+        t = min(t, t1 - 1);
+#pragma unroll
+        for (int a = 0; a < QPW; ++a) {
+          const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
+          b.w[a] = load16(nib + blk * 1024 + loff);
+          b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+        }
+      };
+      auto consume = [&](const TileBuf<QPW>& b) {
+        f32x4 acc = zero4;
+#pragma unroll
+        for (int a = 0; a < QPW; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w4_group(xa[a][j], mfma16x16x32(xa[a][j], neg136, zero4), b.w[a][j], scale_of(b.s[a], j),
+                     acc);
+        return acc;
+      };
+      TileBuf<QPW> A, B;
+      issue(t0, A);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(t0 + 1, B);
+      __builtin_amdgcn_sched_barrier(0);
+      park(part, wave, consume(A));
+      if (nt > 1) park(part, W + wave, consume(B));  // uniform
+      // add the waves' partial sums in wave order and store the gathered rows
+      __syncthreads();
+      const float* pf = reinterpret_cast<const float*>(part);
+      for (int id = threadIdx.x; id < nt * 256; id += blockDim.x) {
+        const int i = id & 3, l = (id >> 2) & 63, tl = id >> 8;
+        const int row = 4 * (l >> 4) + i;
+        const int n = 16 * (t0 + tl) + (l & 15);
+        if (row >= cnt || n >= N) continue;
+        float sum = 0.f;
+        for (int w = 0; w < W; ++w) sum += pf[((tl * W + w) * 64 + l) * 4 + i];
+        y[(size_t)rows[row] * N + n] = sum;
+      }
+    }
+    if (next >= npairs) break;
+    start = next;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -742,6 +873,26 @@ hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int
   const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
   const size_t eb = w4_packed_bytes(N, K);
   const size_t scale_off = (size_t)n_tiles * Q * 1024;
+  int qpw = 0;
+  for (int c : {1, 2, 4})
+    if (qpw == 0 && (Q + c - 1) / c <= short_max_waves(c)) qpw = c;
+  if (qpw > 0) {
+    const int W = (Q + qpw - 1) / qpw;
+    const dim3 grid((n_tiles + kRoutedRun - 1) / kRoutedRun, m * topk);
+#define SVE_ROUTED(Q_)                                                                          \
+  hipLaunchKernelGGL((w4_gemv_routed_short_kernel<Q_>), grid, dim3(64 * W), 0, st,               \
+                     (const uint16_t*)x, x_per_slot, m, ids, topk, (const uint8_t*)packed_all, eb, \
+                     scale_off, E, N, K, Q, n_tiles, y)
+    if (qpw == 1)
+      SVE_ROUTED(1);
+    else if (qpw == 2)
+      SVE_ROUTED(2);
+    else
+      SVE_ROUTED(4);
+#undef SVE_ROUTED
+    return hipGetLastError();
+  }
+  // long K: the ring-pipelined form
   const int tpw = kGemvWaves / gemv_ks(Q);
   const dim3 grid((n_tiles + tpw - 1) / tpw, m * topk);
   hipLaunchKernelGGL(w4_gemv_routed_kernel<1>, grid, dim3(kGemvThreads), 0, st,
