@@ -661,15 +661,17 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_routed_kernel(
 // wave, and walks its run of the expert's row tiles double buffered. Each
 // distinct expert's weights therefore stream through the chip once, spread
 // over many workgroups.
-constexpr int kRoutedRun = 2;        // row tiles per workgroup
+constexpr int kRoutedRun = 2;        // fewest row tiles per workgroup
 constexpr int kRoutedMaxPairs = 256;  // m * topk (16 x 16)
 
 template <int QPW>
 __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_short_kernel(
     const uint16_t* __restrict__ x, int x_per_slot, int m, const int32_t* __restrict__ ids,
     int topk, const uint8_t* __restrict__ packed_all, size_t expert_bytes, size_t scale_off,
-    int E, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
-  __shared__ f32x4 part[kGemvMaxWaves * kRoutedRun * 64];
+    int E, int N, int K, int Q, int n_tiles, int run, int batch, float* __restrict__ y) {
+  // parked partial sums: `batch` tiles of W 1 KB slots (dynamic LDS, sized
+  // by the launcher so that short-K shapes keep several workgroups per CU)
+  extern __shared__ f32x4 part[];
   __shared__ int sid[kRoutedMaxPairs];  // the routing table, read once
   __shared__ int rows[16];
   __shared__ int s_next;
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kb = lane >> 4, r = lane & 15;
   const int G = K >> 5;
-  const int t0 = blockIdx.x * kRoutedRun, t1 = min(n_tiles, t0 + kRoutedRun);
+  const int t0 = blockIdx.x * run, t1 = min(n_tiles, t0 + run);
   if (t0 >= t1) return;
   const int nt = t1 - t0;
   const bool valid = (e >= 0 && e < E);
@@ -759,25 +761,47 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
                      acc);
         return acc;
       };
+      // add the waves' parked partial sums of tiles [tile0, tile0 + k) in
+      // wave order and store the gathered rows
+      auto flush = [&](int tile0, int k) {
+        __syncthreads();
+        const float* pf = reinterpret_cast<const float*>(part);
+        for (int id = threadIdx.x; id < k * 256; id += blockDim.x) {
+          const int i = id & 3, l = (id >> 2) & 63, tl = id >> 8;
+          const int row = 4 * (l >> 4) + i;
+          const int n = 16 * (tile0 + tl) + (l & 15);
+          if (row >= cnt || n >= N) continue;
+          float sum = 0.f;
+          for (int w = 0; w < W; ++w) sum += pf[((tl * W + w) * 64 + l) * 4 + i];
+          y[(size_t)rows[row] * N + n] = sum;
+        }
+        __syncthreads();
+      };
+      // double-buffered walk over the run (as in the dense short kernel)
       TileBuf<QPW> A, B;
       issue(t0, A);
       __builtin_amdgcn_sched_barrier(0);
       issue(t0 + 1, B);
       __builtin_amdgcn_sched_barrier(0);
-      park(part, wave, consume(A));
-      if (nt > 1) park(part, W + wave, consume(B));  // uniform
-      // add the waves' partial sums in wave order and store the gathered rows
-      __syncthreads();
-      const float* pf = reinterpret_cast<const float*>(part);
-      for (int id = threadIdx.x; id < nt * 256; id += blockDim.x) {
-        const int i = id & 3, l = (id >> 2) & 63, tl = id >> 8;
-        const int row = 4 * (l >> 4) + i;
-        const int n = 16 * (t0 + tl) + (l & 15);
-        if (row >= cnt || n >= N) continue;
-        float sum = 0.f;
-        for (int w = 0; w < W; ++w) sum += pf[((tl * W + w) * 64 + l) * 4 + i];
-        y[(size_t)rows[row] * N + n] = sum;
+      int tb = t0;
+      for (int t = t0; t < t1; t += 2) {
+        const f32x4 acc0 = consume(A);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + 2, A);
+        __builtin_amdgcn_sched_barrier(0);
+        park(part, (t - tb) * W + wave, acc0);
+        const f32x4 acc1 = consume(B);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + 3, B);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < t1) park(part, (t + 1 - tb) * W + wave, acc1);
+        const int done = min(t + 2, t1) - tb;
+        if (done + 2 > batch || t + 2 >= t1) {
+          flush(tb, done);
+          tb += done;
+        }
       }
+      (void)nt;
     }
     if (next >= npairs) break;
     start = next;
@@ -873,20 +897,28 @@ hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int
   const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
   const size_t eb = w4_packed_bytes(N, K);
   const size_t scale_off = (size_t)n_tiles * Q * 1024;
+  // (two quads per wave would exceed the 16-wave register budget here)
   int qpw = 0;
-  for (int c : {1, 2, 4})
+  for (int c : {1, 4})
     if (qpw == 0 && (Q + c - 1) / c <= short_max_waves(c)) qpw = c;
   if (qpw > 0) {
     const int W = (Q + qpw - 1) / qpw;
-    const dim3 grid((n_tiles + kRoutedRun - 1) / kRoutedRun, m * topk);
+    // row tiles per workgroup: about 8192 waves in all if every pair slot
+    // owned a distinct expert (two rounds of 16 waves per CU); an even
+    // count, at least two
+    const int npairs = m * topk;
+    int run = (int)(((long long)n_tiles * npairs * W + 8191) / 8192);
+    run = std::max(kRoutedRun, std::min((run + 1) / 2 * 2, n_tiles));
+    // tiles per LDS batch: an even count, at most the run
+    const int batch = std::max(2, std::min((run + 1) / 2 * 2, kGemvPartSlots / W / 2 * 2));
+    const size_t lds = (size_t)batch * W * 64 * sizeof(float) * 4;
+    const dim3 grid((n_tiles + run - 1) / run, npairs);
 #define SVE_ROUTED(Q_)                                                                          \
-  hipLaunchKernelGGL((w4_gemv_routed_short_kernel<Q_>), grid, dim3(64 * W), 0, st,               \
+  hipLaunchKernelGGL((w4_gemv_routed_short_kernel<Q_>), grid, dim3(64 * W), lds, st,             \
                      (const uint16_t*)x, x_per_slot, m, ids, topk, (const uint8_t*)packed_all, eb, \
-                     scale_off, E, N, K, Q, n_tiles, y)
+                     scale_off, E, N, K, Q, n_tiles, run, batch, y)
     if (qpw == 1)
       SVE_ROUTED(1);
-    else if (qpw == 2)
-      SVE_ROUTED(2);
     else
       SVE_ROUTED(4);
 #undef SVE_ROUTED
