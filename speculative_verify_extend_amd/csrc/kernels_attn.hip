@@ -119,6 +119,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
 // row (lane % 16): row statistics need two cross-lane steps only.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
+// word 3 of a raw buffer resource (32-bit data format, no swizzle)
+constexpr int kBufWord3 = 0x00020000;
 
 // swizzled 16-byte chunk position of chunk c in K-tile row `key` (D/8 chunks
 // per row) and in Vt-tile row `d` (8 chunks per row)
@@ -128,6 +130,14 @@ __device__ __forceinline__ int kswz(int key, int c) {
   return c ^ (((key & (CPR - 1)) ^ (((key >> 4) & 1) << 2)) & (CPR - 1));
 }
 __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
+
+// wait until at most N vector-memory requests of this wave are outstanding
+// (lgkm and export counters untouched)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int D, int RT>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
@@ -148,7 +158,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   const int g = prm.g, Hq = prm.Hq, cap = prm.cap;
   const int P = sg.P, m = sg.m, R = m * g;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2, gw = wave & 3;
   const int kb = lane >> 4, col = lane & 15;
 
@@ -159,21 +170,21 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   if (kstart >= kend) return;  // no row of this block sees this split
   const int wg_min_lim = P + wg_row0 / g;
   const int ntiles = (kend - kstart + 63) / 64;
-  const int niter = (ntiles + 1) / 2;  // tile pairs
 
-  int lim[RT], qi[RT], qh[RT];
-  bool rvalid[RT];
+  // packed row of (lane, rt): query row qi, query head qh (recomputed where
+  // needed rather than held through the key loop)
+  auto prow = [&](int rt) { return wg_row0 + gw * 16 * RT + 16 * rt + col; };
+  int lim[RT];
   bf16x8 qreg[RT][DC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int pr = wg_row0 + gw * 16 * RT + 16 * rt + col;
-    rvalid[rt] = pr < R;
-    const int i = rvalid[rt] ? pr / g : 0;
-    qi[rt] = i;
-    qh[rt] = kvh * g + (rvalid[rt] ? pr % g : 0);
-    lim[rt] = rvalid[rt] ? P + i : 0;
+    const int pr = prow(rt);
+    const bool valid = pr < R;
+    const int i = valid ? pr / g : 0;
+    const int qh = kvh * g + (valid ? pr % g : 0);
+    lim[rt] = valid ? P + i : 0;
     // padded rows read a live query row; their outputs are never stored
-    const uint16_t* qrow = sg.q + ((size_t)i * Hq + qh[rt]) * D;
+    const uint16_t* qrow = sg.q + ((size_t)i * Hq + qh) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qreg[rt][dc] = as_bf16x8(load16(qrow + 32 * dc + 8 * kb));
   }
@@ -192,63 +203,56 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   const uint16_t* Vg = sg.Vt + (size_t)kvh * D * cap;
   const float cs = prm.c;
 
-  // per-lane element offsets of the direct loads (fixed for every tile)
-  int koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
+  // Per-lane byte offsets of the direct loads. Step u of a wave covers tile
+  // chunks (gw + 4u)*64 + lane: K rows 4096u bytes further on, with the
+  // swizzle of step u & 1, and Vt rows 64u*cap bytes further on, with the
+  // swizzle of step 0; the step terms are uniform and join the scalar base.
+  uint32_t kloc[2], vloc;
 #pragma unroll
-  for (int u = 0; u < DMA_PER_WAVE; ++u) {
-    const int pos = (gw + 4 * u) * 64 + lane;  // 16-byte chunk index within the tile part
-    const int key = pos / CPR, d = pos >> 3;
-    koff[u] = key * D + kswz<D>(key, pos % CPR) * 8;
-    voff[u] = d * cap + vswz(d, pos & 7) * 8;
+  for (int u = 0; u < 2; ++u) {
+    const int pos = (gw + 4 * u) * 64 + lane;
+    const int key = pos / CPR;
+    kloc[u] = (uint32_t)(key * D + kswz<D>(key, pos % CPR) * 8) * 2u - 4096u * u;
+  }
+  {
+    const int pos = gw * 64 + lane, d = pos >> 3;
+    vloc = (uint32_t)(d * cap + vswz(d, pos & 7) * 8) * 2u;
   }
   // Row blocks walk their tiles from different starting points (rotated by
   // the row block index), so the workgroups sharing a KV head do not all
   // fetch the same tile from L2 at the same moment.
   const int mytiles = (ntiles - grp + 1) / 2;  // tiles of this key group
   auto tile_kt = [&](int t) { return kstart + 64 * (2 * ((t + rb) % max(mytiles, 1)) + grp); };
-  // direct loads of tile `t` of this group into buffer `b`
-  auto dma = [&](int t, int b) {
-    const int kt = tile_kt(t);
-    const uint16_t* kb_ = Kg + (size_t)kt * D;
-    const uint16_t* vb_ = Vg + kt;
+  // direct loads of the K (or Vt) part of tile t into buffer t % 2, through
+  // buffer resources over this KV head's K and Vt (the tile and step terms
+  // are uniform offsets)
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kg), (short)0, cap * D * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vg), (short)0, D * cap * 2, kBufWord3);
+  auto dma_k = [&](int t) {
+    const int base = tile_kt(t) * D * 2;
 #pragma unroll
-    for (int u = 0; u < DMA_PER_WAVE; ++u) {
-      const int step = gw + 4 * u;  // 1 KB step within the tile part
-      __builtin_amdgcn_global_load_lds((const void*)(kb_ + koff[u]),
-                                       (lds_void*)&lds[grp][b][0][step * 512], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vb_ + voff[u]),
-                                       (lds_void*)&lds[grp][b][1][step * 512], 16, 0, 0);
-    }
+    for (int u = 0; u < DMA_PER_WAVE; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc,
+                                               (lds_void*)&lds[grp][t & 1][0][(gw + 4 * u) * 512],
+                                               16, (int)kloc[u & 1], base + 4096 * u, 0, 0);
+  };
+  auto dma_v = [&](int t) {
+    const int base = tile_kt(t) * 2;
+#pragma unroll
+    for (int u = 0; u < DMA_PER_WAVE; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc,
+                                               (lds_void*)&lds[grp][t & 1][1][(gw + 4 * u) * 512],
+                                               16, (int)vloc, base + 64 * u * cap, 0, 0);
   };
 
-  auto compute = [&](int t, int b, auto edge_tag) {
+  f32x4 S[RT][2][2];
+  bf16x8 pb[RT][2];
+  // online softmax of tile t: mask, running max, rescale, bf16 probabilities
+  auto softmax = [&](int t, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int kt = tile_kt(t);
-    const uint16_t* Ks = lds[grp][b][0];
-    const uint16_t* Vs = lds[grp][b][1];
-    f32x4 S[RT][2][2];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) S[rt][c][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int kappa = 32 * c + 8 * (col >> 2) + 4 * sub + (col & 3);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const bf16x8 kop =
-              as_bf16x8(load16(Ks + kappa * D + kswz<D>(kappa, 4 * dc + kb) * 8));
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            S[rt][c][sub] = mfma16x16x32(kop, qreg[rt][dc], S[rt][c][sub]);
-        }
-      }
-    }
-    bf16x8 pb[RT][2];
     bool grow = false;
     float mcand[RT];
 #pragma unroll
@@ -311,6 +315,66 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       }
       lrun[rt] = psum;
     }
+  };
+  // Matrix stage: PV(tpv) (O^T += Vt P^T from tile tpv's Vt part) and/or
+  // QK(tqk) (S^T = K Q^T from tile tqk's K part) as one stream of 16-byte
+  // LDS operand reads, each feeding the two row tiles' products, with the
+  // read for step s+4 issued before the products of step s so that LDS
+  // latency hides behind the matrix pipe. Step order keeps consecutive
+  // products on different accumulators.
+  auto mstage = [&](int tpv, int tqk, auto pv_tag, auto qk_tag) {
+    constexpr bool DO_PV = decltype(pv_tag)::value, DO_QK = decltype(qk_tag)::value;
+    constexpr int NPV = DO_PV ? 2 * DT : 0;  // V operands (c, dt), dt fastest
+    constexpr int NQK = DO_QK ? 4 * DC : 0;  // K operands (dc, c, sub), (c, sub) fastest
+    constexpr int N = NPV + NQK;
+    constexpr int AHEAD = 4;
+    const uint16_t* Vs = lds[grp][tpv & 1][1];
+    const uint16_t* Ks = lds[grp][tqk & 1][0];
+    auto operand = [&](int st) -> bf16x8 {
+      if (st < NPV) {
+        const int c = st / DT, dt = st % DT;
+        const int d = 16 * dt + col;
+        return as_bf16x8(load16(Vs + d * 64 + vswz(d, 4 * c + kb) * 8));
+      }
+      const int q = st - NPV;
+      const int dc = q / 4, c = (q >> 1) & 1, sub = q & 1;
+      const int kappa = 32 * c + 8 * (col >> 2) + 4 * sub + (col & 3);
+      return as_bf16x8(load16(Ks + kappa * D + kswz<D>(kappa, 4 * dc + kb) * 8));
+    };
+    if constexpr (DO_QK) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) S[rt][c][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bf16x8 ring[AHEAD];
+#pragma unroll
+    for (int st = 0; st < AHEAD; ++st) ring[st] = operand(st);
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int st = 0; st < N; ++st) {
+      const bf16x8 op = ring[st % AHEAD];
+      if (st + AHEAD < N) ring[st % AHEAD] = operand(st + AHEAD);
+      if (st < NPV) {
+        const int c = st / DT, dt = st % DT;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) O[rt][dt] = mfma16x16x32(op, pb[rt][c], O[rt][dt]);
+      } else {
+        const int q = st - NPV;
+        const int dc = q / 4, c = (q >> 1) & 1, sub = q & 1;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          S[rt][c][sub] = mfma16x16x32(op, qreg[rt][dc], S[rt][c][sub]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);
+      if (st + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // O^T += Vt P^T for tile t from its Vt part
+  auto pv = [&](int t) {
+    const uint16_t* Vs = lds[grp][t & 1][1];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 16 * dt + col;
@@ -322,23 +386,70 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       }
     }
   };
+  auto stage_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // group G owns tiles 0 .. mytiles-1 of its own sequence
-  if (mytiles > 0) dma(0, 0);
-  __syncthreads();
-  for (int j = 0; j < niter; ++j) {
-    if (j + 1 < mytiles) dma(j + 1, (j + 1) & 1);
-    if (j < mytiles) {
-      // Keys past a row's causal limit only occur in tiles that reach beyond
-      // the smallest limit of the workgroup's rows; only those tiles mask.
-      const int kt = tile_kt(j);
-      if (kt + 63 > wg_min_lim)
-        compute(j, j & 1, std::true_type{});
-      else
-        compute(j, j & 1, std::false_type{});
-    }
-    __syncthreads();
+  // Staged schedule. A key group's stages are
+  //   QK(0) | softmax(0) | PV(0) QK(1) | softmax(1) | ... | softmax(n-1) | PV(n-1)
+  // and group 1 runs one stage behind group 0, so in every stage one wave of
+  // each SIMD issues matrix products while its partner computes
+  // exponentials. A workgroup barrier closes every stage. The K part of tile
+  // j+2 and the Vt part of tile j+1 are requested at the start of
+  // softmax(j) (their buffers were last read in the stage before); the end
+  // of softmax(j) waits only for the requests made two stages earlier,
+  // which are what the next stage reads.
+  constexpr int NV = DMA_PER_WAVE;
+  const int n = mytiles;
+  if (n > 0) {
+    dma_k(0);
+    dma_v(0);
   }
+  if (n > 1) dma_k(1);
+  if (grp == 1) stage_end();  // group 1 starts one stage later
+  if (n > 1)
+    wait_vmem<2 * NV>();  // K(0) in; V(0), K(1) may be in flight
+  else
+    wait_vmem<NV>();
+  stage_end();
+  int nbar = grp + 1;
+  if (n > 0) {
+    mstage(0, 0, std::false_type{}, std::true_type{});
+    stage_end();
+    for (int j = 0; j + 1 < n; ++j) {
+      const bool k2 = j + 2 < n;
+      if (k2) dma_k(j + 2);
+      dma_v(j + 1);
+      // Keys past a row's causal limit only occur in tiles that reach beyond
+      // the smallest limit of the workgroup's rows; only those mask.
+      if (tile_kt(j) + 63 > wg_min_lim)
+        softmax(j, std::true_type{});
+      else
+        softmax(j, std::false_type{});
+      if (k2)
+        wait_vmem<2 * NV>();
+      else
+        wait_vmem<NV>();
+      stage_end();
+      mstage(j, j + 1, std::true_type{}, std::true_type{});
+      stage_end();
+    }
+    if (tile_kt(n - 1) + 63 > wg_min_lim)
+      softmax(n - 1, std::true_type{});
+    else
+      softmax(n - 1, std::false_type{});
+    wait_vmem<0>();
+    stage_end();
+    mstage(n - 1, 0, std::true_type{}, std::false_type{});
+    stage_end();
+    nbar += 2 * n + 1;
+  }
+  // both groups pass the same number of barriers
+  const int n0 = (ntiles + 1) / 2, n1 = ntiles / 2;
+  const int total = max(2 * n0 + 2, 2 * n1 + 3);
+  for (; nbar < total; ++nbar) stage_end();
 
   // merge group 1 into group 0 (same lane = same rows and columns)
   f32x4* xo = reinterpret_cast<f32x4*>(&lds[0][0][0][0]);  // [RT*(DT+1)][256 lanes]
@@ -374,8 +485,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     float l = lrun[rt];
     l += xor_shfl(l, 16);
     l += xor_shfl(l, 32);
-    if (!rvalid[rt]) continue;
-    const size_t orow = ((size_t)qi[rt] * Hq + qh[rt]) * D;
+    const int pr = prow(rt);
+    if (pr >= R) continue;
+    const int qi = pr / g, qh = kvh * g + pr % g;
+    const size_t orow = ((size_t)qi * Hq + qh) * D;
     if (sg.splits == 1) {
       const float inv = 1.f / l;
 #pragma unroll
@@ -391,7 +504,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<f32x4*>(sg.ws_o + wrow + 16 * dt + 4 * kb) = O[rt][dt];
       if (kb == 0) {
-        float* ml = sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 2;
+        float* ml = sg.ws_ml + (((size_t)split * m + qi) * Hq + qh) * 2;
         ml[0] = mref[rt];
         ml[1] = l;
       }
