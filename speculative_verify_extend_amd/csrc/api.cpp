@@ -3,7 +3,7 @@
 // The context owns only host metadata (cached lengths, selected prompts'
 // lengths, LRU ticks). Device memory is the caller's arena:
 //   [prompt tokens: cap int32][slot token mirrors: 4 x cap int32][LCP out]
-//   [split workspace: partial O fp32, (max, sum) fp32][slot 0][slot 1]...
+//   [split workspace: partial o fp16, (max, sum, scale) fp32][slot 0][slot 1]...
 // and each slot holds n_layers x { K [Hkv][cap][D], Vt [Hkv][D][cap] } bf16.
 #include "sve.h"
 
@@ -60,9 +60,9 @@ Layout make_layout(const sve_config* c) {
   L.off_lcp = off;
   off += align_up((size_t)kMaxLcpPairs * 4);
   L.off_ws_o = off;
-  off += align_up((size_t)kMaxSplits * c->max_rows * c->n_q_heads * c->head_dim * 4);
+  off += align_up((size_t)kMaxSplits * c->max_rows * c->n_q_heads * c->head_dim * 2);
   L.off_ws_ml = off;
-  off += align_up((size_t)kMaxSplits * c->max_rows * c->n_q_heads * 2 * 4);
+  off += align_up((size_t)kMaxSplits * c->max_rows * c->n_q_heads * 4 * 4);
   L.fixed = off;
   L.layer_bytes = align_up((size_t)2 * c->n_kv_heads * L.cap * c->head_dim * 2);
   L.slot_bytes = (size_t)c->n_layers * L.layer_bytes;
@@ -99,7 +99,7 @@ struct sve_ctx {
   int32_t* tok() { return (int32_t*)(arena + lay.off_tok); }
   int32_t* slot_tok(int s) { return (int32_t*)(arena + lay.off_slot_tok) + (size_t)s * lay.cap; }
   int32_t* lcp_out() { return (int32_t*)(arena + lay.off_lcp); }
-  float* ws_o() { return (float*)(arena + lay.off_ws_o); }
+  uint16_t* ws_o() { return (uint16_t*)(arena + lay.off_ws_o); }
   float* ws_ml() { return (float*)(arena + lay.off_ws_ml); }
   uint16_t* kbase(int s, int l) {
     return (uint16_t*)(arena + lay.fixed + (size_t)s * lay.slot_bytes + (size_t)l * lay.layer_bytes);
@@ -204,7 +204,7 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     sg.block_begin = blocks;
     sg.row_begin = rows;
     sg.ws_o = c->ws_o() + (size_t)ws_rows * p.Hq * p.D;
-    sg.ws_ml = c->ws_ml() + (size_t)ws_rows * p.Hq * 2;
+    sg.ws_ml = c->ws_ml() + (size_t)ws_rows * p.Hq * 4;
     ws_rows += (long long)S * sg.m;
     blocks += p.Hkv * sg.row_blocks * S;
     rows += sg.m;

@@ -34,6 +34,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // nothing next to the row maximum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Split partials hold a split's normalised output o = O / l (a convex mix of
+// value rows) in fp16, divided by 2^e: e = 0 unless the row's largest |o|
+// reaches 2^15, so the stored values stay inside the fp16 range. fp16 keeps
+// 11 significant bits, four more than the bf16 output.
+__device__ __forceinline__ int partial_exp(float rowmax) {
+  const int k = (int)((__float_as_uint(rowmax) >> 23) & 0xffu) - 127;  // floor(log2) of a normal
+  return max(0, k - 14);
+}
+
 struct SegRef {
   int s, local;
 };
@@ -485,12 +494,23 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     float l = lrun[rt];
     l += xor_shfl(l, 16);
     l += xor_shfl(l, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // largest |o| of the row (its D columns: this lane's tiles, then the
+    // row's four lanes) for the partial's scale
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(O[rt][dt][i]));
+    mx *= inv;
+    mx = fmaxf(mx, xor_shfl(mx, 16));
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    const int ex = partial_exp(mx);
     const int pr = prow(rt);
     if (pr >= R) continue;
     const int qi = pr / g, qh = kvh * g + pr % g;
     const size_t orow = ((size_t)qi * Hq + qh) * D;
     if (sg.splits == 1) {
-      const float inv = 1.f / l;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x2 w;
@@ -499,15 +519,18 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         *reinterpret_cast<u32x2*>(sg.out + orow + 16 * dt + 4 * kb) = w;
       }
     } else {
+      const float f = ldexpf(inv, -ex);
       const size_t wrow = ((size_t)split * m * Hq) * D + orow;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4*>(sg.ws_o + wrow + 16 * dt + 4 * kb) = O[rt][dt];
-      if (kb == 0) {
-        float* ml = sg.ws_ml + (((size_t)split * m + qi) * Hq + qh) * 2;
-        ml[0] = mref[rt];
-        ml[1] = l;
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x2 w;
+        w[0] = pack_f16x2(O[rt][dt][0] * f, O[rt][dt][1] * f);
+        w[1] = pack_f16x2(O[rt][dt][2] * f, O[rt][dt][3] * f);
+        *reinterpret_cast<u32x2*>(sg.ws_o + wrow + 16 * dt + 4 * kb) = w;
       }
+      if (kb == 0)
+        *reinterpret_cast<f32x4*>(sg.ws_ml + (((size_t)split * m + qi) * Hq + qh) * 4) =
+            f32x4{mref[rt], l, ldexpf(1.f, ex), 0.f};
     }
   }
 }
@@ -728,6 +751,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams prm) {
     for (int dt = 0; dt < DT; ++dt) xo[(base + 1 + dt) * 64 + lane] = O[rt][dt];
   }
   __syncthreads();
+  // merged outputs of this wave's d tiles (wave w: tiles w, w+4, ...)
+  constexpr int DPW = (DT + kDecWaves - 1) / kDecWaves;
+  f32x4 ofin[RT][DPW];
+  float Mr[RT], Lr[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float M = -INFINITY;
@@ -746,31 +773,77 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams prm) {
       sw[w] = fast_exp2(mw[w] - Mu);
       L += sw[w] * lw[w];
     }
-    const bool store = rvalid[rt] && k0 <= lim[rt];
-    const size_t orow = ((size_t)qi[rt] * Hq + qh[rt]) * D;
-    for (int dt = wave; dt < DT; dt += kDecWaves) {
+    Mr[rt] = M;
+    Lr[rt] = L;
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int dt = wave + kDecWaves * u;
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      if (dt < DT) {
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        const f32x4 ow = xo[((w * RT + rt) * (DT + 1) + 1 + dt) * 64 + lane];
+        for (int w = 0; w < kDecWaves; ++w) {
+          const f32x4 ow = xo[((w * RT + rt) * (DT + 1) + 1 + dt) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] += sw[w] * ow[i];
-      }
-      if (!store) continue;
-      if (S == 1) {
-        const float inv = 1.f / L;
-        u32x2 w2;
-        w2[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
-        w2[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
-        *reinterpret_cast<u32x2*>(sg.out + orow + 16 * dt + 4 * kb) = w2;
-      } else {
-        *reinterpret_cast<f32x4*>(sg.ws_o + (size_t)split * m * Hq * D + orow + 16 * dt + 4 * kb) =
-            o;
-        if (dt == 0 && kb == 0) {
-          float* ml = sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 2;
-          ml[0] = M;
-          ml[1] = L;
+          for (int i = 0; i < 4; ++i) o[i] += sw[w] * ow[i];
         }
+      }
+      ofin[rt][u] = o;
+    }
+  }
+  if (S > 1) {
+    // largest |o| of each row for the partial's scale: this wave's tiles,
+    // the row's four lanes, then the four waves (through LDS)
+    __shared__ float rmax[kDecWaves][RT][64];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < DPW; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(ofin[rt][u][i]));
+      mx = fmaxf(mx, xor_shfl(mx, 16));
+      mx = fmaxf(mx, xor_shfl(mx, 32));
+      rmax[wave][rt][lane] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) mx = fmaxf(mx, rmax[w][rt][lane]);
+      const float inv = Lr[rt] > 0.f ? 1.f / Lr[rt] : 0.f;
+      const int ex = partial_exp(mx * inv);
+      const float f = ldexpf(inv, -ex);
+      if (!(rvalid[rt] && k0 <= lim[rt])) continue;
+      const size_t orow = ((size_t)qi[rt] * Hq + qh[rt]) * D;
+#pragma unroll
+      for (int u = 0; u < DPW; ++u) {
+        const int dt = wave + kDecWaves * u;
+        if (dt >= DT) continue;
+        u32x2 w2;
+        w2[0] = pack_f16x2(ofin[rt][u][0] * f, ofin[rt][u][1] * f);
+        w2[1] = pack_f16x2(ofin[rt][u][2] * f, ofin[rt][u][3] * f);
+        *reinterpret_cast<u32x2*>(sg.ws_o + (size_t)split * m * Hq * D + orow + 16 * dt + 4 * kb) =
+            w2;
+      }
+      if (wave == 0 && kb == 0)
+        *reinterpret_cast<f32x4*>(sg.ws_ml + (((size_t)split * m + qi[rt]) * Hq + qh[rt]) * 4) =
+            f32x4{Mr[rt], Lr[rt], ldexpf(1.f, ex), 0.f};
+    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (!(rvalid[rt] && k0 <= lim[rt])) continue;
+      const size_t orow = ((size_t)qi[rt] * Hq + qh[rt]) * D;
+      const float inv = 1.f / Lr[rt];
+#pragma unroll
+      for (int u = 0; u < DPW; ++u) {
+        const int dt = wave + kDecWaves * u;
+        if (dt >= DT) continue;
+        u32x2 w2;
+        w2[0] = pack_bf16x2(ofin[rt][u][0] * inv, ofin[rt][u][1] * inv);
+        w2[1] = pack_bf16x2(ofin[rt][u][2] * inv, ofin[rt][u][3] * inv);
+        *reinterpret_cast<u32x2*>(sg.out + orow + 16 * dt + 4 * kb) = w2;
       }
     }
   }
@@ -805,6 +878,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
   __shared__ uint32_t ps[4][kValuRows][32];              // per wave: p pairs
   __shared__ float wm[4][kValuRows], wl[4][kValuRows];
   __shared__ float wo[4][kValuRows][D];
+  __shared__ float fm[kValuRows], fl[kValuRows];  // merged (max, sum) per row
 
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   const SegRef ref = find_seg(prm, L);
@@ -935,6 +1009,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
     for (int j = 0; j < DPL; ++j) wo[wave][r][lane + 64 * j] = oacc[r][j];
   }
   __syncthreads();
+  // merged o = O / l of each (row, column); kept in wo[0] for the partials
   for (int c = threadIdx.x; c < nrows * D; c += 256) {
     const int r = c / D, d = c % D;
     float M = -INFINITY;
@@ -953,19 +1028,40 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
     if (sg.splits == 1) {
       reinterpret_cast<__bf16*>(sg.out)[((size_t)i * Hq + h) * D + d] = (__bf16)(o / l);
     } else {
-      sg.ws_o[(((size_t)split * m + i) * Hq + h) * D + d] = o;
+      wo[0][r][d] = l > 0.f ? o / l : 0.f;  // only this thread reads (r, d)
       if (d == 0) {
-        float* ml = sg.ws_ml + (((size_t)split * m + i) * Hq + h) * 2;
-        ml[0] = M;
-        ml[1] = l;
+        fm[r] = M;
+        fl[r] = l;
       }
     }
+  }
+  if (sg.splits == 1) return;
+  __syncthreads();
+  // one wave per row: the row's largest |o| sets the partial's scale
+  for (int r = wave; r < nrows; r += 4) {
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) mx = fmaxf(mx, fabsf(wo[0][r][lane + 64 * j]));
+    mx = wave_max(mx);
+    const int ex = partial_exp(mx);
+    const int pr = row0 + r;
+    const int i = pr / g, h = kvh * g + pr % g;
+    const size_t base = (((size_t)split * m + i) * Hq + h) * D;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j)
+      sg.ws_o[base + lane + 64 * j] =
+          __builtin_bit_cast(uint16_t, (_Float16)ldexpf(wo[0][r][lane + 64 * j], -ex));
+    if (lane == 0)
+      *reinterpret_cast<f32x4*>(sg.ws_ml + (((size_t)split * m + i) * Hq + h) * 4) =
+          f32x4{fm[r], fl[r], ldexpf(1.f, ex), 0.f};
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split combine: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
-// splits that contain at least one key the row can see, in split order.
+// Split combine: out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s over
+// the splits that contain at least one key the row can see, in split order,
+// with o_s = O_s / l_s the split's normalised output (stored in fp16 times
+// its scale s_s).
 // grid over rows (i, h) of all pieces; 4 columns per thread.
 // ---------------------------------------------------------------------------
 // One wave per (row, q head), four per workgroup. Lane (chunk, part): D/4
@@ -992,24 +1088,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   // decode layout (cached splits + one new-key split): all of them
   const int nvalid =
       sg.tail_split ? sg.splits : min(sg.splits, (sg.P + i) / sg.split_keys + 1);
-  const float* mlp = sg.ws_ml + ((size_t)i * p.Hq + h) * 2;
-  const float* op = sg.ws_o + ((size_t)i * p.Hq + h) * D + c4;
-  const size_t ml_stride = (size_t)sg.m * p.Hq * 2, o_stride = (size_t)sg.m * p.Hq * D;
+  const float* mlp = sg.ws_ml + ((size_t)i * p.Hq + h) * 4;
+  const uint16_t* op = sg.ws_o + ((size_t)i * p.Hq + h) * D + c4;
+  const size_t ml_stride = (size_t)sg.m * p.Hq * 4, o_stride = (size_t)sg.m * p.Hq * D;
+  // running (max, sum, sum of weighted outputs); a split's weight is
+  // 2^(m_s - M) l_s and its stored value o_s / s_s
   float M = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int b0 = 0; b0 * PARTS < nvalid; b0 += BATCH) {
-    float2 ml[BATCH];
-    f32x4 o[BATCH];
+    f32x4 ml[BATCH];
+    u32x2 o[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const size_t q = (size_t)min((b0 + u) * PARTS + part, nvalid - 1);
-      ml[u] = *reinterpret_cast<const float2*>(mlp + q * ml_stride);
-      o[u] = *reinterpret_cast<const f32x4*>(op + q * o_stride);
+      ml[u] = *reinterpret_cast<const f32x4*>(mlp + q * ml_stride);
+      o[u] = *reinterpret_cast<const u32x2*>(op + q * o_stride);
     }
     float Mb = M;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
-      if ((b0 + u) * PARTS + part < nvalid) Mb = fmaxf(Mb, ml[u].x);
+      if ((b0 + u) * PARTS + part < nvalid) Mb = fmaxf(Mb, ml[u][0]);
     const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
     l *= r;
 #pragma unroll
@@ -1018,10 +1116,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       if ((b0 + u) * PARTS + part < nvalid) {
-        const float sc = fast_exp2(ml[u].x - M);
-        l += sc * ml[u].y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += sc * o[u][e];
+        const float sc = fast_exp2(ml[u][0] - M);
+        const float wl = sc * ml[u][1];
+        const float wo = wl * ml[u][2];
+        l += wl;
+        acc[0] += wo * f16_bits_to_f32(o[u][0] & 0xFFFFu);
+        acc[1] += wo * f16_bits_to_f32(o[u][0] >> 16);
+        acc[2] += wo * f16_bits_to_f32(o[u][1] & 0xFFFFu);
+        acc[3] += wo * f16_bits_to_f32(o[u][1] >> 16);
       }
     }
   }

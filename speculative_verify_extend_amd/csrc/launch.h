@@ -29,8 +29,12 @@ struct AttnSeg {
   const uint16_t* nk;  // new rows [m][Hkv][D]
   const uint16_t* nv;
   uint16_t* out;       // [m][Hq][D]
-  float* ws_o;         // [splits][m][Hq][D] (this piece's part of the workspace)
-  float* ws_ml;        // [splits][m][Hq][2]
+  // split partials (this piece's part of the workspace): the split's
+  // normalised output o = O / l in fp16, divided by the power of two s
+  // (s = 1 unless the row's largest |o| reaches 2^15), and per (split, row,
+  // head) the running max m (log2 units), the sum l and s
+  uint16_t* ws_o;      // [splits][m][Hq][D] fp16
+  float* ws_ml;        // [splits][m][Hq][4]: m, l, s, 0
   int P, m;
   int row_blocks;      // per KV head
   int splits, split_keys;
