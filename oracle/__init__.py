@@ -13,7 +13,10 @@ Modules (each function cites the passage of the source pages it follows):
   * ``attention`` — extend-prefill attention (m new rows against a cached
                     prefix plus themselves), vectorised and brute-force forms;
   * ``slots``     — the resident KV-slot store and the slot-selection rule;
-  * ``fit``       — the fixed + marginal-per-row cost fit of verify time.
+  * ``fit``       — the fixed + marginal-per-row cost fit of verify time;
+  * ``verify``    — greedy acceptance of a verify step, the KV rollback it
+                    implies, the rolling-acceptance gate and the break-even
+                    acceptance of the cost model.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` to closed forms,
 invariants, brute force or independent library routines; none is left

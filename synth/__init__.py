@@ -182,3 +182,36 @@ def attention_case(seed: int, hq: int, hkv: int, d: int, prefix: int, m: int):
     gs = rng(seed, 2)
     q, k, v = attention_rows(gs, m, hq, hkv, d)
     return dict(q_prefix=qp, k_prefix=kp, v_prefix=vp, q=q, k=k, v=v)
+
+
+# --------------------------------------------------------------------------
+# verify logits
+# --------------------------------------------------------------------------
+
+VERIFY_VOCAB = 151936  # a Qwen-family vocabulary size; the pages' models use one
+
+
+def verify_case(seed: int, m: int, vocab: int, n_match: int, tie: bool = False):
+    """Logits and drafts of one verify step of m = k + 1 rows.
+
+    logits: fp32 [m][vocab] drawn N(0,1), then one entry per row set to 8.0 at
+    a random id (the planted top entry); with ``tie`` a second random id of
+    the row gets the same 8.0. drafts: int32 [m-1], equal to row i's first
+    planted id for i < n_match and a different random id after that.
+    Returns (logits, drafts, planted ids [m][1 or 2])."""
+    g = rng(seed, 7)
+    logits = g.standard_normal((m, vocab), dtype=np.float32)
+    npl = 2 if tie else 1
+    planted = np.stack([g.choice(vocab, size=npl, replace=False) for _ in range(m)])
+    for i in range(m):
+        logits[i, planted[i]] = np.float32(8.0)
+    drafts = np.empty(m - 1, dtype=np.int32)
+    for i in range(m - 1):
+        if i < n_match:
+            drafts[i] = planted[i, 0]
+        else:
+            d = int(g.integers(0, vocab))
+            while d in planted[i]:
+                d = int(g.integers(0, vocab))
+            drafts[i] = d
+    return logits, drafts, planted
