@@ -409,6 +409,33 @@ def verify_sweep(backlog, layers=ROT_LAYERS, reps=3, graphs=True):
 
 
 # ---------------------------------------------------------------------------
+# verify acceptance (greedy argmax over a Qwen-family vocabulary)
+# ---------------------------------------------------------------------------
+
+def verify_accept_sweep(backlog, copies=8, reps=3):
+    """Per m = k+1: time of one sve_verify_accept call (both kernels, HIP
+    events around the call) on fp32 logits [m][151936], rotated over
+    `copies` buffers; GB/s on the m*V*4 logit bytes."""
+    vocab = synth.VERIFY_VOCAB
+    res = {}
+    for m in range(1, 9):
+        cases = [synth.verify_case(90 + i, m, vocab, (m - 1) // 2) for i in range(copies)]
+        lg = [torch.from_numpy(c[0]).cuda() for c in cases]
+        dr = [torch.from_numpy(c[1]).cuda() if m > 1 else None for c in cases]
+        ws = torch.empty(sve.verify_workspace_bytes(m, vocab), dtype=torch.uint8, device="cuda")
+        out = [torch.empty(2 + m, dtype=torch.int32, device="cuda") for _ in range(copies)]
+        calls = [lambda i=i: sve.verify_accept(lg[i], dr[i], out[i], ws) for i in range(copies)]
+        d = []
+        for _ in range(reps):
+            d += bracket(calls, backlog)
+        us = float(np.median(d)) * 1e3
+        res[m] = {"us": us, "GBps": m * vocab * 4 / (us * 1e-6) / 1e9,
+                  "accepted": int(out[0][0].item())}
+        del lg, dr, ws, out
+    return res
+
+
+# ---------------------------------------------------------------------------
 # MoE routed GEMV (35B-A3B-like)
 # ---------------------------------------------------------------------------
 
@@ -659,6 +686,17 @@ def main():
             out["verify_attention"]["forced_" + path + "_attn_kernel_us"] = {
                 m: r2(v["attn_kernel_us"]) for m, v in vp.items()}
         os.environ.pop("SVE_MFMA_MIN_ROWS", None)
+        log("verify accept")
+        va = verify_accept_sweep(backlog)
+        out["verify_accept"] = {
+            "workload": "greedy acceptance of m = k+1 verify rows over a 151936-id vocabulary "
+                        "(fp32 logits, 8 rotated copies): per-row argmax + acceptance scan",
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "achieved": round(max(v["GBps"] for v in va.values()), 1),
+                         "frac": round(max(v["GBps"] for v in va.values()) / HBM_PEAK_GBS, 4),
+                         "what": "best m of 1..8, logit bytes / call time (two launches)"},
+            "per_m": {m: {"us": r2(v["us"]), "GBps": round(v["GBps"], 1),
+                          "accepted": v["accepted"]} for m, v in va.items()}}
         log("moe sweep")
         mo = moe_sweep(backlog)
         a3, b3 = fit(list(mo), [mo[m]["us"] for m in mo])

@@ -188,6 +188,66 @@ int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int
                          int32_t topk, const void* packed_all, int32_t E, int32_t N, int32_t K,
                          float* y, void* hip_stream);
 
+/* ---- speculative verify: acceptance, rollback and gate --------------------
+ * thinkspread, "The economics of speculative decoding: +41% on 9B, break-even
+ * on 35B": a draft head proposes k tokens, one pass over m = k + 1 rows
+ * checks them and the runtime keeps the ones that were right (opening
+ * section); when the rolling acceptance drops under a threshold the runtime
+ * falls back to ordinary decoding ("Gating: enable it only where it pays");
+ * verify(m) = a + b*m prices whether it pays ("Closing the ledger"). */
+
+#define SVE_VERIFY_MAX_ROWS 16
+#define SVE_GATE_MAX_WINDOW 64
+
+/* Device workspace bytes sve_verify_accept needs for m rows of V logits
+ * (0 if m or V is out of range). */
+size_t sve_verify_workspace_bytes(int32_t m, int32_t V);
+
+/* Greedy acceptance of one verify step. Row i of `logits` holds the target
+ * model's scores for the token after input i, where the inputs are the last
+ * accepted token and the k = m - 1 drafts. Draft i+1 is kept while it equals
+ * row i's argmax (ties: the lowest id; a NaN counts as larger than any
+ * number); the row after the last kept draft gives the next token. The
+ * caller then keeps P + accepted + 1 cached positions of the slot the m rows
+ * were appended to (sve_kv_truncate), P being its length before the verify.
+ *   logits: device fp32 [m][V], rows contiguous; 1 <= m <= SVE_VERIFY_MAX_ROWS,
+ *           V >= 1.
+ *   draft: device int32 [m-1] (may be NULL when m == 1).
+ *   result: device int32 [2 + m]: accepted drafts (0..m-1), the next token,
+ *           then the argmax of every row.
+ *   workspace: caller-owned device memory of at least
+ *              sve_verify_workspace_bytes(m, V) bytes.
+ * ASYNC on hip_stream (two kernel launches). Errors: SVE_E_ARG, SVE_E_HIP. */
+int sve_verify_accept(const float* logits, int32_t m, int32_t V, const int32_t* draft,
+                      int32_t* result, void* workspace, size_t workspace_bytes,
+                      void* hip_stream);
+
+/* Rolling-acceptance gate of one request (host only). Each verify step
+ * records its accepted count; the rolling acceptance is (sum of the last
+ * `window` counts) / (k * those steps), fewer steps at the start; once it is
+ * below min_accept the gate closes and the depth stays 0 for the request. */
+typedef struct {
+  int32_t k;          /* draft depth for the next step; 0 once closed */
+  int32_t window;     /* 1..SVE_GATE_MAX_WINDOW */
+  double min_accept;  /* e.g. 0.60 */
+  int32_t steps;      /* steps recorded */
+  int32_t accepted[SVE_GATE_MAX_WINDOW];  /* ring of the recent counts */
+} sve_spec_gate;
+
+/* 0 <= k <= SVE_VERIFY_MAX_ROWS - 1, 0 <= min_accept <= 1, window in range.
+ * Errors: SVE_E_ARG. */
+int sve_spec_gate_init(sve_spec_gate* gate, int32_t k, double min_accept, int32_t window);
+
+/* Record a step that kept `accepted` (0..k) of k drafts; *k_next = the depth
+ * for the next step. A closed gate ignores `accepted`. Errors: SVE_E_ARG. */
+int sve_spec_gate_step(sve_spec_gate* gate, int32_t accepted, int32_t* k_next);
+
+/* Break-even per-position acceptance of depth k under verify(m) = a + b*m:
+ * the alpha in [0, 1] with (1 + alpha + ... + alpha^k) * (a + b) = a +
+ * b*(k+1), the draft head's own cost left out; 0 for k = 0, 1 when even
+ * alpha = 1 does not pay, -1 for a + b <= 0, b < 0 or k < 0. */
+double sve_spec_break_even(double a, double b, int32_t k);
+
 /* ---- measurement probes (not part of the computation) ---------------------
  * Plain streaming read and plain copy of device memory, used to measure the
  * achievable HBM bandwidth beside the published peak and to calibrate the

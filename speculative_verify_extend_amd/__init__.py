@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import SveError, check
 
 __all__ = ["KVSlots", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m",
-           "w4_gemv_m_routed", "probe_read", "probe_copy", "SveError", "load_library"]
+           "w4_gemv_m_routed", "verify_workspace_bytes", "verify_accept", "SpecGate",
+           "spec_break_even", "probe_read", "probe_copy", "SveError", "load_library"]
 
 
 def load_library():
@@ -214,6 +215,60 @@ def w4_gemv_m_routed(x: torch.Tensor, expert_ids: torch.Tensor, packed_all: torc
     check(lib.sve_w4_gemv_m_routed(_ptr(x), int(bool(x_per_slot)), m, _ptr(expert_ids), topk,
                                    _ptr(packed_all), n_experts, n, k, _ptr(y), _stream()))
     return y
+
+
+def verify_workspace_bytes(m: int, vocab: int) -> int:
+    """Device workspace bytes of verify_accept for m rows of `vocab` logits."""
+    return int(_lib.load().sve_verify_workspace_bytes(m, vocab))
+
+
+def verify_accept(logits: torch.Tensor, draft: torch.Tensor | None,
+                  result: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Greedy acceptance of one verify step (asynchronous).
+
+    logits: fp32 [m][V] (rows for the last accepted token and the k = m-1
+    drafts); draft: int32 [m-1] (None when m == 1). Returns int32 [2 + m]:
+    accepted drafts, next token, per-row argmax."""
+    lib = _lib.load()
+    m, vocab = logits.shape
+    _need(logits, torch.float32, (m, vocab), "logits")
+    if m > 1 or draft is not None:
+        _need(draft, torch.int32, (m - 1,), "draft")
+    ws_bytes = lib.sve_verify_workspace_bytes(m, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=logits.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    if result is None:
+        result = torch.empty(2 + m, dtype=torch.int32, device=logits.device)
+    _need(result, torch.int32, (2 + m,), "result")
+    check(lib.sve_verify_accept(_ptr(logits), m, vocab,
+                                None if draft is None else _ptr(draft), _ptr(result),
+                                _ptr(workspace), workspace.numel(), _stream()))
+    return result
+
+
+class SpecGate:
+    """Rolling-acceptance gate of one request (host-side, libsve)."""
+
+    def __init__(self, k: int, min_accept: float = 0.60, window: int = 8):
+        self._g = _lib.SpecGate()
+        check(_lib.load().sve_spec_gate_init(C.byref(self._g), k, float(min_accept), window))
+
+    @property
+    def k(self) -> int:
+        return int(self._g.k)
+
+    def step(self, accepted: int) -> int:
+        """Record a verify step that kept `accepted` drafts; returns the next depth."""
+        k_next = C.c_int32(0)
+        check(_lib.load().sve_spec_gate_step(C.byref(self._g), int(accepted), C.byref(k_next)))
+        return int(k_next.value)
+
+
+def spec_break_even(a: float, b: float, k: int) -> float:
+    """Break-even per-position acceptance of depth k under verify(m) = a + b*m."""
+    return float(_lib.load().sve_spec_break_even(float(a), float(b), int(k)))
 
 
 def probe_read(src: torch.Tensor, blocks: int, unroll: int = 4) -> torch.Tensor:

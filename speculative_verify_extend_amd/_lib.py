@@ -36,6 +36,20 @@ class SveConfig(C.Structure):
     ]
 
 
+SVE_VERIFY_MAX_ROWS = 16
+SVE_GATE_MAX_WINDOW = 64
+
+
+class SpecGate(C.Structure):
+    _fields_ = [
+        ("k", C.c_int32),
+        ("window", C.c_int32),
+        ("min_accept", C.c_double),
+        ("steps", C.c_int32),
+        ("accepted", C.c_int32 * SVE_GATE_MAX_WINDOW),
+    ]
+
+
 _P = C.c_void_p
 _I = C.c_int32
 _SIGS = {
@@ -61,6 +75,11 @@ _SIGS = {
     "sve_timing_start": (C.c_int, [_P, _I]),
     "sve_timing_read": (C.c_int, [_P, C.POINTER(C.c_float), C.POINTER(C.c_float),
                                   C.POINTER(C.c_float), C.POINTER(_I)]),
+    "sve_verify_workspace_bytes": (C.c_size_t, [_I, _I]),
+    "sve_verify_accept": (C.c_int, [_P, _I, _I, _P, _P, _P, C.c_size_t, _P]),
+    "sve_spec_gate_init": (C.c_int, [_P, _I, C.c_double, _I]),
+    "sve_spec_gate_step": (C.c_int, [_P, _I, C.POINTER(_I)]),
+    "sve_spec_break_even": (C.c_double, [C.c_double, C.c_double, _I]),
     "sve_strerror": (C.c_char_p, [C.c_int]),
     "sve_last_error": (C.c_char_p, [_P]),
 }

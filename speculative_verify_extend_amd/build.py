@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libsve.so")
 ARCH = os.environ.get("SVE_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "kernels_w4.hip", "kernels_attn.hip", "kernels_slot.hip",
-           "kernels_probe.hip"]
+           "kernels_probe.hip", "kernels_verify.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

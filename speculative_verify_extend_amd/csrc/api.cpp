@@ -580,6 +580,78 @@ int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int
   return SVE_OK;
 }
 
+size_t sve_verify_workspace_bytes(int32_t m, int32_t V) {
+  if (m < 1 || m > SVE_VERIFY_MAX_ROWS || V < 1) return 0;
+  return verify_workspace_bytes(m, V);
+}
+
+int sve_verify_accept(const float* logits, int32_t m, int32_t V, const int32_t* draft,
+                      int32_t* result, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  if (m < 1 || m > SVE_VERIFY_MAX_ROWS) return fail(nullptr, SVE_E_ARG, "m must be 1..16");
+  if (V < 1) return fail(nullptr, SVE_E_ARG, "V must be >= 1");
+  if (!logits || !result || !workspace || (m > 1 && !draft))
+    return fail(nullptr, SVE_E_ARG, "null pointer");
+  if (workspace_bytes < verify_workspace_bytes(m, V))
+    return fail(nullptr, SVE_E_ARG, "workspace smaller than sve_verify_workspace_bytes");
+  SVE_HIP(nullptr, launch_verify_accept(logits, m, V, draft, result, workspace,
+                                        (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_spec_gate_init(sve_spec_gate* g, int32_t k, double min_accept, int32_t window) {
+  if (!g) return fail(nullptr, SVE_E_ARG, "null gate");
+  if (k < 0 || k > SVE_VERIFY_MAX_ROWS - 1) return fail(nullptr, SVE_E_ARG, "k must be 0..15");
+  if (!(min_accept >= 0.0 && min_accept <= 1.0))
+    return fail(nullptr, SVE_E_ARG, "min_accept must be in [0, 1]");
+  if (window < 1 || window > SVE_GATE_MAX_WINDOW)
+    return fail(nullptr, SVE_E_ARG, "window must be 1..64");
+  memset(g, 0, sizeof(*g));
+  g->k = k;
+  g->window = window;
+  g->min_accept = min_accept;
+  return SVE_OK;
+}
+
+int sve_spec_gate_step(sve_spec_gate* g, int32_t accepted, int32_t* k_next) {
+  if (!g || !k_next) return fail(nullptr, SVE_E_ARG, "null pointer");
+  if (g->window < 1 || g->window > SVE_GATE_MAX_WINDOW || g->k < 0)
+    return fail(nullptr, SVE_E_ARG, "gate not initialised");
+  if (g->k > 0) {
+    if (accepted < 0 || accepted > g->k) return fail(nullptr, SVE_E_ARG, "accepted must be 0..k");
+    g->accepted[g->steps % g->window] = accepted;
+    ++g->steps;
+    const int n = std::min(g->steps, g->window);
+    long long sum = 0;
+    for (int i = 0; i < n; ++i) sum += g->accepted[i];
+    // (sum of counts) / (k * steps), one rounding
+    if ((double)sum / ((double)g->k * (double)n) < g->min_accept) g->k = 0;
+  }
+  *k_next = g->k;
+  return SVE_OK;
+}
+
+double sve_spec_break_even(double a, double b, int32_t k) {
+  if (!(a + b > 0.0) || !(b >= 0.0) || k < 0) return -1.0;
+  if (k == 0) return 0.0;
+  auto tokens = [k](double alpha) {
+    double t = 0.0;
+    for (int i = 0; i <= k; ++i) t += std::pow(alpha, i);
+    return t;
+  };
+  const double need = (a + b * (k + 1)) / (a + b);
+  if (tokens(1.0) < need) return 1.0;
+  double lo = 0.0, hi = 1.0;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (tokens(mid) < need)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
 int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll, void* sink,
                    void* hip_stream) {
   if (!src || !sink || bytes == 0 || bytes % 16) return fail(nullptr, SVE_E_ARG, "bad probe buffer");

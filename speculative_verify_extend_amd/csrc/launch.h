@@ -65,6 +65,12 @@ hipError_t launch_attn_combine(const AttnParams& p, hipStream_t st);
 hipError_t launch_kv_read(const uint16_t* K, const uint16_t* Vt, int Hkv, int D, int cap,
                           int start, int len, uint16_t* k_out, uint16_t* v_out, hipStream_t st);
 
+// ---- speculative verify -------------------------------------------------------------
+constexpr int kVerifyMaxRows = 16;
+size_t verify_workspace_bytes(int m, int V);
+hipError_t launch_verify_accept(const float* logits, int m, int V, const int32_t* draft,
+                                int32_t* result, void* workspace, hipStream_t st);
+
 // ---- measurement probes ------------------------------------------------------------
 hipError_t launch_probe_read(const void* src, size_t bytes, int blocks, int unroll, void* sink,
                              hipStream_t st);
