@@ -26,8 +26,9 @@ Readings (the pages do not spell these out):
     last accepted input plus the accepted drafts, so the cache is cut back to
     P + accepted + 1 positions.
   * acceptance of a step = accepted / k; the rolling acceptance is the mean
-    over the last `window` steps (fewer at the start), and once it is below
-    the threshold the request stops speculating (k = 0) for good.
+    over the last `window` steps (fewer at the start), taken as (sum of the
+    accepted counts) / (k * steps), and once it is below the threshold the
+    request stops speculating (k = 0) for good.
   * the break-even acceptance of depth k under verify(m) = a + b*m, with a
     per-position acceptance alpha that is the same at every depth, is the
     alpha where the expected tokens per verify step, 1 + alpha + ... +
@@ -35,8 +36,6 @@ Readings (the pages do not spell these out):
     step; the draft head's own cost is left out.
 """
 from __future__ import annotations
-
-import math
 
 import numpy as np
 
@@ -100,11 +99,11 @@ class RollingGate:
         self.k = k
         self.min_accept = min_accept
         self.window = window
-        self.rates: list[float] = []
+        self.accepted: list[int] = []
 
     def rolling(self) -> float:
-        recent = self.rates[-self.window:]
-        return math.fsum(recent) / len(recent) if recent else 1.0
+        recent = self.accepted[-self.window:]
+        return sum(recent) / (self.k * len(recent)) if recent else 1.0
 
     def step(self, accepted: int) -> int:
         """Record one verify step with `accepted` of k drafts kept; returns
@@ -112,7 +111,7 @@ class RollingGate:
         if self.k == 0:
             return 0
         assert 0 <= accepted <= self.k
-        self.rates.append(accepted / self.k)
+        self.accepted.append(int(accepted))
         if self.rolling() < self.min_accept:
             self.k = 0
         return self.k
