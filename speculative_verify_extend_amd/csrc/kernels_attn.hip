@@ -148,7 +148,9 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int D, int RT>
+// ONE: the call has a single piece (its fields load without first finding
+// the piece, one scalar round trip less)
+template <int D, int RT, bool ONE>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   constexpr int DC = D / 32;
   constexpr int DT = D / 16;
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][2][TILE];  // [group][buf][K|Vt]
 
   const int L = xcd_linear(blockIdx.x, gridDim.x);
-  const SegRef ref = find_seg(prm, L);
-  const AttnSeg& sg = prm.seg[ref.s];
+  const SegRef ref = ONE ? SegRef{0, L} : find_seg(prm, L);
+  const AttnSeg& sg = prm.seg[ONE ? 0 : ref.s];
   const int split = ref.local % sg.splits;
   const int rest = ref.local / sg.splits;
   const int rb = rest % sg.row_blocks;
@@ -558,15 +560,16 @@ constexpr int kDecWaves = 4;
 constexpr int kDecRowsPerBlock = 32;
 constexpr int kDecMaxNew = 64;  // new keys per call on this path (m <= 64)
 
-template <int D, int RT, int NS>
+template <int D, int RT, int NS, bool ONE>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams prm) {
   constexpr int DC = D / 32, DT = D / 16, CPR = D / 8;
   constexpr int XO = kDecWaves * RT * (DT + 1) * 64;  // f32x4 slots: wave states
   static_assert(XO * 16 >= D * kDecMaxNew * 2, "new-row staging fits the merge area");
   __shared__ f32x4 xo[XO];
 
-  const SegRef ref = find_seg(prm, xcd_linear(blockIdx.x, gridDim.x));
-  const AttnSeg& sg = prm.seg[ref.s];
+  const int L = xcd_linear(blockIdx.x, gridDim.x);
+  const SegRef ref = ONE ? SegRef{0, L} : find_seg(prm, L);
+  const AttnSeg& sg = prm.seg[ONE ? 0 : ref.s];
   const int S = sg.splits;
   const int split = ref.local % S;
   const int rest = ref.local / S;
@@ -1069,16 +1072,18 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
 // t+2P, ... (P = 256/D), loading BATCH of them per round, and the parts are
 // then merged in part order through lane shuffles. Every (row, head) is
 // merged in the same fixed order whatever the launch shape.
-template <int D, int BATCH>
+template <int D, int BATCH, bool ONE>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   constexpr int CH = D / 4, PARTS = 64 / CH;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (grow, h): one per wave
   if (row >= p.total_rows * p.Hq) return;
   const int grow = row / p.Hq, h = row % p.Hq;
   int s = 0;
+  if constexpr (!ONE) {
 #pragma unroll
-  for (int j = 1; j < kMaxSeg; ++j)
-    if (j < p.nseg && grow >= p.seg[j].row_begin) s = j;
+    for (int j = 1; j < kMaxSeg; ++j)
+      if (j < p.nseg && grow >= p.seg[j].row_begin) s = j;
+  }
   const AttnSeg& sg = p.seg[s];
   if (sg.splits == 1) return;
   const int lane = threadIdx.x & 63;
@@ -1187,35 +1192,53 @@ hipError_t launch_kv_append(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool ONE>
 static void launch_decode(const AttnParams& p, int rt, int ns, hipStream_t st) {
   const dim3 grid(p.total_blocks), block(256);
   switch (rt * 2 + ns) {
-    case 3: hipLaunchKernelGGL((attn_decode_kernel<D, 1, 1>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 1, 2>), grid, block, 0, st, p); break;
-    case 5: hipLaunchKernelGGL((attn_decode_kernel<D, 2, 1>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((attn_decode_kernel<D, 2, 2>), grid, block, 0, st, p); break;
+    case 3: hipLaunchKernelGGL((attn_decode_kernel<D, 1, 1, ONE>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 1, 2, ONE>), grid, block, 0, st, p); break;
+    case 5: hipLaunchKernelGGL((attn_decode_kernel<D, 2, 1, ONE>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_decode_kernel<D, 2, 2, ONE>), grid, block, 0, st, p); break;
   }
+}
+
+template <int D, bool ONE>
+static void launch_mfma(const AttnParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, 2, ONE>), dim3(p.total_blocks), dim3(512), 0, st, p);
+}
+
+template <int D, bool ONE>
+static void launch_combine(const AttnParams& p, bool wide, hipStream_t st) {
+  const int blocks = (p.total_rows * p.Hq + 3) / 4;
+  if (wide)
+    hipLaunchKernelGGL((attn_combine_kernel<D, 16, ONE>), dim3(blocks), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, 4, ONE>), dim3(blocks), dim3(256), 0, st, p);
 }
 
 hipError_t launch_attn(const AttnParams& p, int path, hipStream_t st) {
   if (p.total_blocks == 0) return hipSuccess;
   const dim3 grid(p.total_blocks), block(256);
   if (path == kPathDecode) {
+    const bool one = p.nseg == 1;
     if (p.D == 128)
-      launch_decode<128>(p, p.dec_rt, p.dec_ns, st);
+      one ? launch_decode<128, true>(p, p.dec_rt, p.dec_ns, st)
+          : launch_decode<128, false>(p, p.dec_rt, p.dec_ns, st);
     else
-      launch_decode<64>(p, p.dec_rt, p.dec_ns, st);
+      one ? launch_decode<64, true>(p, p.dec_rt, p.dec_ns, st)
+          : launch_decode<64, false>(p, p.dec_rt, p.dec_ns, st);
   } else if (path == kPathValu) {
     if (p.D == 128)
       hipLaunchKernelGGL(attn_valu_kernel<128>, grid, block, 0, st, p);
     else
       hipLaunchKernelGGL(attn_valu_kernel<64>, grid, block, 0, st, p);
   } else {
+    const bool one = p.nseg == 1;
     if (p.D == 128)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(512), 0, st, p);
+      one ? launch_mfma<128, true>(p, st) : launch_mfma<128, false>(p, st);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(512), 0, st, p);
+      one ? launch_mfma<64, true>(p, st) : launch_mfma<64, false>(p, st);
   }
   return hipGetLastError();
 }
@@ -1226,20 +1249,13 @@ hipError_t launch_attn_combine(const AttnParams& p, hipStream_t st) {
   if (!any) return hipSuccess;
   int max_s = 0;
   for (int s = 0; s < p.nseg; ++s) max_s = p.seg[s].splits > max_s ? p.seg[s].splits : max_s;
-  const int blocks = (p.total_rows * p.Hq + 3) / 4;
   // splits loaded per part and round: few splits -> short rounds
   const bool wide = max_s > (p.D == 128 ? 8 : 16);
-  if (p.D == 128) {
-    if (wide)
-      hipLaunchKernelGGL((attn_combine_kernel<128, 16>), dim3(blocks), dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<128, 4>), dim3(blocks), dim3(256), 0, st, p);
-  } else {
-    if (wide)
-      hipLaunchKernelGGL((attn_combine_kernel<64, 16>), dim3(blocks), dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<64, 4>), dim3(blocks), dim3(256), 0, st, p);
-  }
+  const bool one = p.nseg == 1;
+  if (p.D == 128)
+    one ? launch_combine<128, true>(p, wide, st) : launch_combine<128, false>(p, wide, st);
+  else
+    one ? launch_combine<64, true>(p, wide, st) : launch_combine<64, false>(p, wide, st);
   return hipGetLastError();
 }
 
