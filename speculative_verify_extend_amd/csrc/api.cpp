@@ -174,6 +174,9 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
   const long long ws_cap = (long long)kMaxSplits * c->cfg.max_rows;  // workspace rows
   long long ws_rows = 0;
   int blocks = 0, rows = 0;
+  // MFMA path: the attention kernel reads the new rows from the call's
+  // inputs and appends them itself
+  const bool fused = path == kPathMfma && env_int("SVE_FUSED_APPEND", 1) != 0;
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
     const bool dec = path == kPathDecode;
@@ -201,6 +204,20 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     sg.splits = S;
     sg.split_keys = sk;
     sg.tail_split = dec ? 1 : 0;
+    sg.new_tile0 = -1;
+    if (fused) {
+      // MFMA path: the tiles from the one holding P on form the last split,
+      // read from the call's rows (and the store below P) and appended by
+      // the kernel; the S-1 other splits share the whole cached tiles
+      const int nt0 = sg.P / 64;
+      S = std::max(1, std::min(S, nt0 + 1));
+      const int tps = S > 1 ? (nt0 + S - 2) / (S - 1) : 1;
+      if (S > 1) S = (nt0 + tps - 1) / tps + 1;
+      sg.splits = S;
+      sg.split_keys = 64 * tps;
+      sg.tail_split = 1;  // every split holds keys each row sees
+      sg.new_tile0 = nt0;
+    }
     sg.block_begin = blocks;
     sg.row_begin = rows;
     sg.ws_o = c->ws_o() + (size_t)ws_rows * p.Hq * p.D;
@@ -276,7 +293,10 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
   if (c->timed_used < c->timed_max) ev = &c->tev[4 * (size_t)c->timed_used++];
   if (ev) SVE_HIP(c, hipEventRecord(ev[0], c->stream));
   hipError_t e = hipSuccess;
-  if (path != kPathDecode) {  // the decode kernel appends its rows itself
+  // the decode kernel, and the MFMA kernel with new tiles, append their rows
+  bool need_append = false;
+  for (int s = 0; s < p.nseg; ++s) need_append |= path != kPathDecode && p.seg[s].new_tile0 < 0;
+  if (need_append) {
     e = launch_kv_append(p, c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "kv_append launch");
   }

@@ -72,6 +72,7 @@ constexpr int kAppendRows = 16;
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
   const AttnSeg& sg = p.seg[blockIdx.z];
+  if (sg.new_tile0 >= 0) return;  // the attention kernel appends this piece
   const int i0 = blockIdx.x * kAppendRows;
   if (i0 >= sg.m) return;
   const int h = blockIdx.y, Hkv = p.Hkv, cap = p.cap;
@@ -176,11 +177,25 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
 
   const int wg_row0 = rb * 64 * RT;
   const int wg_last = min(R - 1, wg_row0 + 64 * RT - 1);
-  const int kstart = split * sg.split_keys;
-  const int kend = min(P + wg_last / g + 1, kstart + sg.split_keys);
-  if (kstart >= kend) return;  // no row of this block sees this split
+  // 64-key tiles [64T, 64T+64); a split is a run of split_keys / 64 of them.
+  // With new_tile0 >= 0 the last split is every tile from new_tile0 = P / 64
+  // on (every tile, when it is the only split): those from new_tile0 on go
+  // through the epilogue, which reads keys at or past P from the call's rows
+  // and appends them. The other tiles come from the store through the staged
+  // loop.
+  const int nt0 = sg.new_tile0;
+  const bool fused = nt0 >= 0;
+  const int tps = sg.split_keys / 64;
+  const int t_rows = (P + wg_last / g) / 64 + 1;  // tiles any row of the block sees
+  const bool last_new = fused && split == sg.splits - 1;
+  const int t_begin = last_new ? (sg.splits == 1 ? 0 : nt0) : split * tps;
+  const int t_end = last_new ? t_rows : min(min(t_begin + tps, t_rows), fused ? nt0 : INT_MAX);
+  if (t_begin >= t_end) return;  // no row of this block sees this split
   const int wg_min_lim = P + wg_row0 / g;
-  const int ntiles = (kend - kstart + 63) / 64;
+  const int t_cend = fused ? max(t_begin, min(t_end, nt0)) : t_end;
+  const int ntiles = t_cend - t_begin;  // staged loop
+  const int nnew = t_end - t_cend;      // epilogue
+  const int kstart = 64 * t_begin;
 
   // packed row of (lane, rt): query row qi, query head qh (recomputed where
   // needed rather than held through the key loop)
@@ -261,9 +276,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   f32x4 S[RT][2][2];
   bf16x8 pb[RT][2];
   // online softmax of tile t: mask, running max, rescale, bf16 probabilities
-  auto softmax = [&](int t, auto edge_tag) {
+  auto softmax = [&](int kt, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const int kt = tile_kt(t);
     bool grow = false;
     float mcand[RT];
 #pragma unroll
@@ -383,20 +397,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       if (st + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // O^T += Vt P^T for tile t from its Vt part
-  auto pv = [&](int t) {
-    const uint16_t* Vs = lds[grp][t & 1][1];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + col;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 vop = as_bf16x8(load16(Vs + d * 64 + vswz(d, 4 * c + kb) * 8));
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) O[rt][dt] = mfma16x16x32(vop, pb[rt][c], O[rt][dt]);
-      }
-    }
-  };
   auto stage_end = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
@@ -436,9 +436,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       // Keys past a row's causal limit only occur in tiles that reach beyond
       // the smallest limit of the workgroup's rows; only those mask.
       if (tile_kt(j) + 63 > wg_min_lim)
-        softmax(j, std::true_type{});
+        softmax(tile_kt(j), std::true_type{});
       else
-        softmax(j, std::false_type{});
+        softmax(tile_kt(j), std::false_type{});
       if (k2)
         wait_vmem<2 * NV>();
       else
@@ -448,9 +448,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       stage_end();
     }
     if (tile_kt(n - 1) + 63 > wg_min_lim)
-      softmax(n - 1, std::true_type{});
+      softmax(tile_kt(n - 1), std::true_type{});
     else
-      softmax(n - 1, std::false_type{});
+      softmax(tile_kt(n - 1), std::false_type{});
     wait_vmem<0>();
     stage_end();
     mstage(n - 1, 0, std::true_type{}, std::false_type{});
@@ -461,6 +461,111 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   const int n0 = (ntiles + 1) / 2, n1 = ntiles / 2;
   const int total = max(2 * n0 + 2, 2 * n1 + 3);
   for (; nbar < total; ++nbar) stage_end();
+
+  if (nnew > 0) {
+    // Tiles holding new keys, two per round (group G takes tile 2r + G).
+    // K: each 16-byte piece from the store below P and from the call's rows
+    // at or past P, straight into LDS in the K-tile layout (round r uses
+    // buffer r % 2's K part). V: the store's Vt pieces whose keys are below P
+    // (only in the tile holding P) straight into buffer 1's V part (Vt-tile
+    // layout); the call's V rows into buffer 0's V part (16-byte chunk c of
+    // row key at chunk c ^ (key % CPR)), transposed from there into buffer
+    // 1's V part (overwriting the store's values at or past P in the piece
+    // holding P). Reads past row m-1 of the call return zeros. The requests
+    // of round r+1 go out once round r's V rows are transposed, so they
+    // overlap round r's products. The workgroup of the last row block sees
+    // every new key and also copies the new rows into the store (positions
+    // P .. P+m-1); no other workgroup of the call reads those positions
+    // except as masked keys.
+    const int Hkv = prm.Hkv;
+    const int new_bytes = ((m - 1) * Hkv + 1) * D * 2;
+    const __amdgpu_buffer_rsrc_t nkrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(sg.nk + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t nvrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(sg.nv + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
+    const bool append = rb == sg.row_blocks - 1;
+    uint16_t* Kw = const_cast<uint16_t*>(Kg);
+    uint16_t* Vw = const_cast<uint16_t*>(Vg);
+    const int gt = gw * 64 + lane;  // thread within the key group
+    constexpr int ITEMS = CPR / 4;  // 16-byte pieces per thread per tile part
+    uint16_t* Vr = lds[grp][0][1];  // the call's V rows as loaded
+    uint16_t* Vs = lds[grp][1][1];  // Vt-tile layout
+    auto new_tile_key0 = [&](int r) { return 64 * (t_cend + r + grp); };
+    // requests of round r (this group's tile, if it has one)
+    auto requests = [&](int r) {
+      if (r + grp >= nnew) return;
+      const int kt = new_tile_key0(r);
+      uint16_t* Ks = lds[grp][(r >> 1) & 1][0];
+#pragma unroll
+      for (int u = 0; u < DMA_PER_WAVE; ++u) {
+        const int pos = (gw + 4 * u) * 64 + lane;
+        lds_void* dk = (lds_void*)&Ks[(gw + 4 * u) * 512];
+        lds_void* dvr = (lds_void*)&Vr[(gw + 4 * u) * 512];
+        lds_void* dvs = (lds_void*)&Vs[(gw + 4 * u) * 512];
+        {  // K piece (key, slot): chunk kswz(key, slot) of key kt + key
+          const int key = pos / CPR, slot = pos % CPR, k = kt + key;
+          const int ch = kswz<D>(key, slot);
+          if (k < P)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, dk, 16, (k * D + ch * 8) * 2, 0, 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                nkrsrc, dk, 16, ((k - P) * Hkv * D + ch * 8) * 2, 0, 0, 0);
+          // V row piece of the same (key, slot) for keys at or past P
+          if (k >= P)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                nvrsrc, dvr, 16, ((k - P) * Hkv * D + (slot ^ (key % CPR)) * 8) * 2, 0, 0, 0);
+        }
+        if (kt < P) {  // Vt piece (d, slot), when its first key is cached
+          const int d = pos >> 3, k8 = kt + 8 * vswz(d, pos & 7);
+          if (k8 < P)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, dvs, 16, (d * cap + k8) * 2, 0, 0, 0);
+        }
+      }
+    };
+    // rounds use buffer (r / 2) % 2's K part: r counts tiles, two per round
+    requests(0);
+    for (int r0 = 0; r0 < nnew; r0 += 2) {
+      const bool has = r0 + grp < nnew;
+      const int kt = new_tile_key0(r0);
+      const uint16_t* Ks = lds[grp][(r0 >> 1) & 1][0];
+      wait_vmem<0>();
+      __syncthreads();
+      if (has) {
+        // transpose the keys at or past P: lane = key, so the 2-byte writes
+        // of one column are contiguous; the appending workgroup stores the
+        // same values into the store
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+          const int item = gt + 256 * u, key = item & 63, c = item >> 6, k = kt + key;
+          if (k >= P) {
+            const u32x4 v = load16(Vr + key * D + (c ^ (key % CPR)) * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int d = 8 * c + e;
+              const uint16_t x = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+              Vs[d * 64 + vswz(d, key >> 3) * 8 + (key & 7)] = x;
+              if (append && k < P + m) Vw[(size_t)d * cap + k] = x;
+            }
+          }
+        }
+        if (append) {
+          for (int it = gt; it < 64 * CPR; it += 256) {
+            const int key = it / CPR, c = it % CPR, k = kt + key;
+            if (k >= P && k < P + m)
+              store16(Kw + (size_t)k * D + c * 8, load16(Ks + key * D + kswz<D>(key, c) * 8));
+          }
+        }
+      }
+      __syncthreads();
+      requests(r0 + 2);  // into the other K buffer and the now free row buffer
+      if (has) {
+        mstage(0, (r0 >> 1) & 1, std::false_type{}, std::true_type{});
+        softmax(kt, std::true_type{});
+        mstage(1, 0, std::true_type{}, std::false_type{});
+      }
+      __syncthreads();
+    }
+  }
 
   // merge group 1 into group 0 (same lane = same rows and columns)
   f32x4* xo = reinterpret_cast<f32x4*>(&lds[0][0][0][0]);  // [RT*(DT+1)][256 lanes]

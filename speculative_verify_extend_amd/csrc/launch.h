@@ -39,6 +39,13 @@ struct AttnSeg {
   int row_blocks;      // per KV head
   int splits, split_keys;
   int tail_split;      // decode layout: splits-1 cached splits of split_keys, then [P, P+m)
+  // MFMA path: first 64-key tile [64t, 64t+64) that holds new keys (P / 64).
+  // With new_tile0 >= 0 the piece's splits-1 first splits hold split_keys
+  // cached keys each (below 64 * new_tile0) and the last split every tile
+  // from new_tile0 on, whose keys at or past P the attention kernel reads
+  // from nk/nv and appends itself. -1: every key is in the store, appended
+  // beforehand, and the splits cut [0, P+m) evenly.
+  int new_tile0;
   int block_begin;     // first linear workgroup of this piece
   int row_begin;       // first output row of this piece in a combined launch
 };

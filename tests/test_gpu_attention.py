@@ -136,6 +136,26 @@ def test_turn9_full_size():
     assert np.abs(got - want).max() <= ATTN_TOL
 
 
+@pytest.mark.parametrize("case", [(28, 4, 128, 1664, 254), (28, 4, 128, 1668, 254),
+                                  (8, 2, 128, 63, 300), (4, 1, 64, 130, 129),
+                                  (8, 2, 128, 0, 200), (8, 2, 128, 700, 21)],
+                         ids=lambda c: "h%d-%d-d%d-P%d-m%d" % c)
+def test_in_kernel_append_matches_separate_append(case):
+    """MFMA path: the attention kernel reads the new rows from the call's
+    inputs and appends them itself (the default), or a separate append
+    kernel writes them first. Both match the oracle, and the cached rows
+    they leave are the appended rows, bit for bit."""
+    hq, hkv, d, P, m = case
+    for fused in (1, 0):
+        announce(f"in-kernel append={fused} {case}")
+        with env(SVE_FUSED_APPEND=fused):
+            got, want, c, st = _run_case(hq, hkv, d, P, m, "mfma", seed=13)
+        assert np.abs(got - want).max() <= ATTN_TOL
+        kk, vv = st.kv_read(0, 0, 0, P + m)
+        assert np.array_equal(host_bits(kk), np.concatenate([c["k_prefix"], c["k"]]))
+        assert np.array_equal(host_bits(vv), np.concatenate([c["v_prefix"], c["v"]]))
+
+
 @pytest.mark.parametrize("m", list(range(1, 9)))
 def test_verify_full_size(m):
     """Speculative verify: 2048 cached + m rows, 32 q / 8 KV heads, D 128, on
