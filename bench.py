@@ -628,6 +628,8 @@ def main():
                 "timing": "HIP events recorded by the library on its stream around the kernel, "
                           f"averaged over {calls} eager calls",
                 "other_kernels_us": {"kv_append": r2(append_us), "combine": r2(combine_us)}}
+    if append_us == 0.0:
+        roofline["other_kernels_us"]["kv_append"] = "none: the attention kernel appends the rows"
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tok/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -267,8 +267,10 @@ int sve_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, voi
  * library without a system-scope fence, so they add no cache write-back to
  * the timed kernels. sve_timing_read waits for the last recorded event, writes the
  * summed durations in milliseconds of each kernel over the timed calls and
- * their count, destroys the events and ends timing (a combine that a call
- * does not need counts as 0). Not for calls under graph capture.
+ * their count, destroys the events and ends timing (a kernel that a call
+ * does not launch counts as 0: the separate append on the paths whose
+ * attention kernel appends its rows itself, the combine of an unsplit
+ * call). Not for calls under graph capture.
  *   1 <= n_calls <= 65536. Errors: SVE_E_ARG, SVE_E_STATE (start while
  *   started, read while not started), SVE_E_HIP. */
 int sve_timing_start(sve_ctx* ctx, int32_t n_calls);

@@ -94,6 +94,8 @@ struct sve_ctx {
   // kernel timing: 4 events per timed extend call (before the KV append,
   // after it, after the attention kernel, after the combine kernel)
   std::vector<hipEvent_t> tev;
+  // per timed call: bit k set when kernel k (append, attention, combine) ran
+  std::vector<uint8_t> tran;
   int timed_max = 0, timed_used = 0;
 
   int32_t* tok() { return (int32_t*)(arena + lay.off_tok); }
@@ -290,12 +292,20 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
   int path = kPathMfma;
   plan_attention(c, p, path);
   hipEvent_t* ev = nullptr;
-  if (c->timed_used < c->timed_max) ev = &c->tev[4 * (size_t)c->timed_used++];
+  uint8_t* ran = nullptr;
+  if (c->timed_used < c->timed_max) {
+    ev = &c->tev[4 * (size_t)c->timed_used];
+    ran = &c->tran[c->timed_used++];
+  }
   if (ev) SVE_HIP(c, hipEventRecord(ev[0], c->stream));
   hipError_t e = hipSuccess;
   // the decode kernel, and the MFMA kernel with new tiles, append their rows
-  bool need_append = false;
-  for (int s = 0; s < p.nseg; ++s) need_append |= path != kPathDecode && p.seg[s].new_tile0 < 0;
+  bool need_append = false, need_combine = false;
+  for (int s = 0; s < p.nseg; ++s) {
+    need_append |= path != kPathDecode && p.seg[s].new_tile0 < 0;
+    need_combine |= p.seg[s].splits > 1 && p.seg[s].m > 0;
+  }
+  if (ran) *ran = (uint8_t)((need_append ? 1 : 0) | 2 | (need_combine ? 4 : 0));
   if (need_append) {
     e = launch_kv_append(p, c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "kv_append launch");
@@ -369,6 +379,7 @@ int sve_timing_start(sve_ctx* c, int32_t n_calls) {
   if (n_calls < 1 || n_calls > 65536) return fail(c, SVE_E_ARG, "n_calls must be 1..65536");
   if (c->timed_max) return fail(c, SVE_E_STATE, "timing already started");
   c->tev.assign(4 * (size_t)n_calls, nullptr);
+  c->tran.assign((size_t)n_calls, 0);
   for (size_t i = 0; i < c->tev.size(); ++i) {
     // no system-scope fence at the events: a cache write-back there would be
     // timed as part of the neighbouring kernels
@@ -394,6 +405,9 @@ int sve_timing_read(sve_ctx* c, float* append_ms, float* attn_ms, float* combine
   if (c->timed_used > 0) err = hipEventSynchronize(c->tev[4 * (size_t)c->timed_used - 1]);
   for (int i = 0; i < c->timed_used && err == hipSuccess; ++i)
     for (int k = 0; k < 3 && err == hipSuccess; ++k) {
+      // a kernel the call did not launch counts as 0: an empty event bracket
+      // still reads a few microseconds on an eager stream
+      if (!(c->tran[i] >> k & 1)) continue;
       float ms = 0.f;
       err = hipEventElapsedTime(&ms, c->tev[4 * (size_t)i + k], c->tev[4 * (size_t)i + k + 1]);
       acc[k] += ms;
@@ -401,6 +415,7 @@ int sve_timing_read(sve_ctx* c, float* append_ms, float* attn_ms, float* combine
   const int used = c->timed_used;
   for (hipEvent_t e : c->tev) (void)hipEventDestroy(e);
   c->tev.clear();
+  c->tran.clear();
   c->timed_max = c->timed_used = 0;
   if (err != hipSuccess) return hip_fail(c, err, "reading timing events");
   *append_ms = (float)acc[0];

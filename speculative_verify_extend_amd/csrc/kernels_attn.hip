@@ -486,7 +486,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     const bool append = rb == sg.row_blocks - 1;
     uint16_t* Kw = const_cast<uint16_t*>(Kg);
     uint16_t* Vw = const_cast<uint16_t*>(Vg);
-    const int gt = gw * 64 + lane;  // thread within the key group
+    // the lane index taken afresh: offsets built from it here are not merged
+    // with the prologue's, which would keep them live through the key loop
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 63;
+    const int gt = gw * 64 + ln;  // thread within the key group
     constexpr int ITEMS = CPR / 4;  // 16-byte pieces per thread per tile part
     uint16_t* Vr = lds[grp][0][1];  // the call's V rows as loaded
     uint16_t* Vs = lds[grp][1][1];  // Vt-tile layout
@@ -498,15 +501,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       uint16_t* Ks = lds[grp][(r >> 1) & 1][0];
 #pragma unroll
       for (int u = 0; u < DMA_PER_WAVE; ++u) {
-        const int pos = (gw + 4 * u) * 64 + lane;
+        const int pos = (gw + 4 * u) * 64 + ln;
         lds_void* dk = (lds_void*)&Ks[(gw + 4 * u) * 512];
         lds_void* dvr = (lds_void*)&Vr[(gw + 4 * u) * 512];
         lds_void* dvs = (lds_void*)&Vs[(gw + 4 * u) * 512];
         {  // K piece (key, slot): chunk kswz(key, slot) of key kt + key
           const int key = pos / CPR, slot = pos % CPR, k = kt + key;
           const int ch = kswz<D>(key, slot);
-          if (k < P)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, dk, 16, (k * D + ch * 8) * 2, 0, 0, 0);
+          if (k < P)  // the same piece as the key loop's direct loads
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, dk, 16, (int)kloc[u & 1],
+                                                     kt * D * 2 + 4096 * u, 0, 0);
           else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 nkrsrc, dk, 16, ((k - P) * Hkv * D + ch * 8) * 2, 0, 0, 0);
@@ -517,8 +521,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         }
         if (kt < P) {  // Vt piece (d, slot), when its first key is cached
           const int d = pos >> 3, k8 = kt + 8 * vswz(d, pos & 7);
-          if (k8 < P)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, dvs, 16, (d * cap + k8) * 2, 0, 0, 0);
+          if (k8 < P)  // the same piece as the key loop's direct loads
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, dvs, 16, (int)vloc,
+                                                     kt * 2 + 64 * u * cap, 0, 0);
         }
       }
     };

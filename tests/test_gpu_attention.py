@@ -333,8 +333,9 @@ def test_batched_matches_single_slot_calls():
 
 def test_kernel_timing_records_each_call():
     """Timing events around the three kernels of each timed call: positive
-    attention time, a count capped at the requested calls, state errors, and
-    results unchanged by timing."""
+    attention time, a count capped at the requested calls, state errors,
+    results unchanged by timing, and 0 for an append the attention kernel
+    does itself."""
     hq, hkv, d, P, m = 28, 4, 128, 600, 40
     c = synth.attention_case(11, hq, hkv, d, P, m)
     st = _store(hq, hkv, d, P + m + 64, P + m)
@@ -354,5 +355,11 @@ def test_kernel_timing_records_each_call():
         assert torch.equal(st.extend_attn(0, 0, q, k, v), ref)
     t = st.timing_read()
     assert t["calls"] == 3
-    assert t["attn_ms"] > 0 and t["append_ms"] > 0 and t["combine_ms"] >= 0
+    assert t["attn_ms"] > 0 and t["append_ms"] == 0 and t["combine_ms"] >= 0
+    with env(SVE_FUSED_APPEND=0):  # the separate append kernel
+        st.timing_start(1)
+        st.kv_truncate(0, P)
+        st.extend_attn(0, 0, q, k, v)  # its own split plan: not bitwise ref
+        t0 = st.timing_read()
+    assert t0["calls"] == 1 and t0["append_ms"] > 0 and t0["attn_ms"] > 0
     assert t["attn_ms"] < 3 * 10.0  # milliseconds: a sanity bound, not a speed check
