@@ -151,6 +151,9 @@ __device__ __forceinline__ void wait_vmem() {
 
 // ONE: the call has a single piece (its fields load without first finding
 // the piece, one scalar round trip less)
+// row-block workgroups of the last split that append the call's rows
+constexpr int kAppendBlocks = 4;
+
 template <int D, int RT, bool ONE>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   constexpr int DC = D / 32;
@@ -422,8 +425,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   if (grp == 1) stage_end();  // group 1 starts one stage later
   if (n > 1)
     wait_vmem<2 * NV>();  // K(0) in; V(0), K(1) may be in flight
-  else
+  else if (n == 1)
     wait_vmem<NV>();
+  // (with no staged tile the query loads stay in flight into the epilogue,
+  // beside its first tile requests)
   stage_end();
   int nbar = grp + 1;
   if (n > 0) {
@@ -473,9 +478,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     // 1's V part (overwriting the store's values at or past P in the piece
     // holding P). Reads past row m-1 of the call return zeros. The requests
     // of round r+1 go out once round r's V rows are transposed, so they
-    // overlap round r's products. The workgroup of the last row block sees
-    // every new key and also copies the new rows into the store (positions
-    // P .. P+m-1); no other workgroup of the call reads those positions
+    // overlap round r's products. After the rounds, the workgroups of the
+    // first row blocks (the ones with the fewest new tiles) copy the call's
+    // rows into the store (positions P .. P+m-1), 64-key tiles dealt out
+    // among them; no other workgroup of the call reads those positions
     // except as masked keys.
     const int Hkv = prm.Hkv;
     const int new_bytes = ((m - 1) * Hkv + 1) * D * 2;
@@ -483,13 +489,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         const_cast<uint16_t*>(sg.nk + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
     const __amdgpu_buffer_rsrc_t nvrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(sg.nv + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
-    const bool append = rb == sg.row_blocks - 1;
     uint16_t* Kw = const_cast<uint16_t*>(Kg);
     uint16_t* Vw = const_cast<uint16_t*>(Vg);
     // the lane index taken afresh: offsets built from it here are not merged
     // with the prologue's, which would keep them live through the key loop
     const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 63;
     const int gt = gw * 64 + ln;  // thread within the key group
+    const int wt = wave * 64 + ln;  // thread within the workgroup
     constexpr int ITEMS = CPR / 4;  // 16-byte pieces per thread per tile part
     uint16_t* Vr = lds[grp][0][1];  // the call's V rows as loaded
     uint16_t* Vs = lds[grp][1][1];  // Vt-tile layout
@@ -537,8 +543,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       __syncthreads();
       if (has) {
         // transpose the keys at or past P: lane = key, so the 2-byte writes
-        // of one column are contiguous; the appending workgroup stores the
-        // same values into the store
+        // of one column are contiguous
 #pragma unroll
         for (int u = 0; u < ITEMS; ++u) {
           const int item = gt + 256 * u, key = item & 63, c = item >> 6, k = kt + key;
@@ -549,15 +554,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
               const int d = 8 * c + e;
               const uint16_t x = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
               Vs[d * 64 + vswz(d, key >> 3) * 8 + (key & 7)] = x;
-              if (append && k < P + m) Vw[(size_t)d * cap + k] = x;
             }
-          }
-        }
-        if (append) {
-          for (int it = gt; it < 64 * CPR; it += 256) {
-            const int key = it / CPR, c = it % CPR, k = kt + key;
-            if (k >= P && k < P + m)
-              store16(Kw + (size_t)k * D + c * 8, load16(Ks + key * D + kswz<D>(key, c) * 8));
           }
         }
       }
@@ -569,6 +566,53 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         mstage(1, 0, std::true_type{}, std::false_type{});
       }
       __syncthreads();
+    }
+
+    // Append: workgroup rb < A takes the 64-key tiles T0 + rb, T0 + rb + A,
+    // ... of the new range. K rows are copied as they are; V rows go into
+    // LDS as [key][D + 2] (odd dword stride: the column reads below meet
+    // distinct banks) and leave as 16-byte pieces of 8 keys of one column,
+    // key by key in the pieces holding P or P+m.
+    const int A = min(sg.row_blocks, kAppendBlocks);
+    if (rb < A) {
+      constexpr int VST = D + 2;
+      uint16_t* Va = &lds[0][0][0][0];  // [64][VST]
+      const uint16_t* nkh = sg.nk + (size_t)kvh * D;
+      const uint16_t* nvh = sg.nv + (size_t)kvh * D;
+      const int T0 = P / 64, T1 = (P + m - 1) / 64;
+      for (int T = T0 + rb; T <= T1; T += A) {
+        for (int it = wt; it < 64 * CPR; it += 512) {
+          const int key = it / CPR, c = it % CPR, k = 64 * T + key;
+          if (k >= P && k < P + m) {
+            const size_t src = (size_t)(k - P) * Hkv * D + c * 8;
+            store16(Kw + (size_t)k * D + c * 8, load16(nkh + src));
+            const u32x4 v = load16(nvh + src);
+            uint32_t* row = reinterpret_cast<uint32_t*>(Va + key * VST + c * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) row[e] = v[e];
+          }
+        }
+        __syncthreads();
+        for (int it = wt; it < D * 8; it += 512) {
+          const int j = it & 7, d = it >> 3, k8 = 64 * T + 8 * j;
+          if (k8 + 8 <= P || k8 >= P + m) continue;
+          uint16_t x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = Va[(8 * j + e) * VST + d];
+          uint16_t* dst = Vw + (size_t)d * cap + k8;
+          if (k8 >= P && k8 + 8 <= P + m) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (uint32_t)x[2 * e] | ((uint32_t)x[2 * e + 1] << 16);
+            store16(dst, w);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (k8 + e >= P && k8 + e < P + m) dst[e] = x[e];
+          }
+        }
+        __syncthreads();
+      }
     }
   }
 
