@@ -136,6 +136,79 @@ int hip_fail(const sve_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(ctx, e_, #expr); \
   } while (0)
 
+// MFMA path. Split s of a piece holds the 64-key tiles [s, s+1) * tps, and
+// row block rb (128 packed rows) gets a workgroup for split s only when its
+// last row sees a key there: the first such row block is g * X / 128 with
+// X = 64 * s * tps - P (row i sees keys up to P + i). Every workgroup then
+// holds at most tps tiles and none is empty. tps is the smallest value that
+// keeps the grid within one round of workgroups on the 256 compute units
+// (and at most 16 splits, what the workspace holds per row).
+int mfma_first_block(int X, int g) { return X > 0 ? (int)(((long long)g * X) / 128) : 0; }
+
+int mfma_head_blocks(const AttnSeg& sg, int g, int tps, int* splits) {
+  const int S = sg.m > 0 ? ((sg.P + sg.m - 1) / 64 + 1 + tps - 1) / tps : 0;
+  int hb = 0;
+  for (int s = 0; s < S; ++s) hb += sg.row_blocks - mfma_first_block(64 * s * tps - sg.P, g);
+  if (splits) *splits = S;
+  return hb;
+}
+
+void plan_mfma(sve_ctx* c, AttnParams& p) {
+  constexpr int kTarget = 256;
+  const int g = p.g;
+  int tmax = 1;
+  for (int s = 0; s < p.nseg; ++s)
+    if (p.seg[s].m > 0) tmax = std::max(tmax, (p.seg[s].P + p.seg[s].m - 1) / 64 + 1);
+  int tps = std::max(1, (tmax + kMaxSplits - 1) / kMaxSplits);
+  const int forced = env_int("SVE_KV_SPLIT", 0);
+  if (forced > 0) {
+    tps = std::max(tps, (tmax + forced - 1) / forced);
+  } else {
+    for (;; ++tps) {
+      long long blocks = 0;
+      for (int s = 0; s < p.nseg; ++s) blocks += (long long)p.Hkv * mfma_head_blocks(p.seg[s], g, tps, nullptr);
+      if (blocks <= kTarget || tps >= tmax) break;
+    }
+  }
+  // the attention kernel reads the new rows from the call's inputs; they
+  // are appended by the combine kernel (split pieces) or by the attention
+  // kernel itself (unsplit pieces)
+  const bool fused = env_int("SVE_FUSED_APPEND", 1) != 0;
+  long long ws_rows = 0;
+  int blocks = 0, rows = 0, app = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    AttnSeg& sg = p.seg[s];
+    int S = 0;
+    sg.head_blocks = mfma_head_blocks(sg, g, tps, &S);
+    sg.splits = std::max(S, 1);
+    sg.split_keys = 64 * tps;
+    sg.tail_split = 0;
+    sg.new_tile0 = fused ? sg.P / 64 : -1;
+    sg.append_begin = app;
+    sg.append_blocks = fused && sg.splits > 1 && sg.m > 0
+                           ? p.Hkv * ((sg.P + sg.m - 1) / 64 - sg.P / 64 + 1) * (p.D / 32)
+                           : 0;
+    app += sg.append_blocks;
+    sg.block_begin = blocks;
+    sg.row_begin = rows;
+    sg.ws_o = c->ws_o() + (size_t)ws_rows * p.Hq * p.D;
+    sg.ws_ml = c->ws_ml() + (size_t)ws_rows * p.Hq * 4;
+    ws_rows += (long long)sg.splits * sg.m;
+    blocks += p.Hkv * sg.head_blocks;
+    rows += sg.m;
+  }
+  p.total_blocks = blocks;
+  p.total_rows = rows;
+  p.append_total = app;
+  if (log_on()) {
+    fprintf(stderr, "[sve] extend: path=mfma pieces=%d blocks=%d tiles/split=%d append=%d", p.nseg,
+            blocks, tps, app);
+    for (int s = 0; s < p.nseg; ++s)
+      fprintf(stderr, " (P=%d m=%d splits=%d)", p.seg[s].P, p.seg[s].m, p.seg[s].splits);
+    fprintf(stderr, "\n");
+  }
+}
+
 // Choose the path, row blocks and key splits of every piece of a call.
 //   decode: every piece has at most 64 packed rows (m*g) per KV head; a
 //           workgroup covers 32 packed rows and a key split of whole
@@ -169,6 +242,10 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     p.seg[s].row_blocks = (p.seg[s].m * g + rpb - 1) / rpb;
     base += p.Hkv * p.seg[s].row_blocks;
   }
+  if (path == kPathMfma) {
+    plan_mfma(c, p);
+    return;
+  }
   const int target = path == kPathValu ? 512 : 256;
   const int unit = path == kPathDecode ? 128 : 64;  // split length granule (keys)
   const int max_splits = path == kPathDecode ? kMaxDecodeSplits : kMaxSplits;
@@ -176,9 +253,6 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
   const long long ws_cap = (long long)kMaxSplits * c->cfg.max_rows;  // workspace rows
   long long ws_rows = 0;
   int blocks = 0, rows = 0;
-  // MFMA path: the attention kernel reads the new rows from the call's
-  // inputs and appends them itself
-  const bool fused = path == kPathMfma && env_int("SVE_FUSED_APPEND", 1) != 0;
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
     const bool dec = path == kPathDecode;
@@ -207,19 +281,8 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     sg.split_keys = sk;
     sg.tail_split = dec ? 1 : 0;
     sg.new_tile0 = -1;
-    if (fused) {
-      // MFMA path: the tiles from the one holding P on form the last split,
-      // read from the call's rows (and the store below P) and appended by
-      // the kernel; the S-1 other splits share the whole cached tiles
-      const int nt0 = sg.P / 64;
-      S = std::max(1, std::min(S, nt0 + 1));
-      const int tps = S > 1 ? (nt0 + S - 2) / (S - 1) : 1;
-      if (S > 1) S = (nt0 + tps - 1) / tps + 1;
-      sg.splits = S;
-      sg.split_keys = 64 * tps;
-      sg.tail_split = 1;  // every split holds keys each row sees
-      sg.new_tile0 = nt0;
-    }
+    sg.head_blocks = sg.row_blocks * S;
+    sg.append_blocks = sg.append_begin = 0;
     sg.block_begin = blocks;
     sg.row_begin = rows;
     sg.ws_o = c->ws_o() + (size_t)ws_rows * p.Hq * p.D;

@@ -166,12 +166,25 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   const int L = xcd_linear(blockIdx.x, gridDim.x);
   const SegRef ref = ONE ? SegRef{0, L} : find_seg(prm, L);
   const AttnSeg& sg = prm.seg[ONE ? 0 : ref.s];
-  const int split = ref.local % sg.splits;
-  const int rest = ref.local / sg.splits;
-  const int rb = rest % sg.row_blocks;
-  const int kvh = rest / sg.row_blocks;
   const int g = prm.g, Hq = prm.Hq, cap = prm.cap;
   const int P = sg.P, m = sg.m, R = m * g;
+  // split-major within a KV head: split s has a workgroup for each row block
+  // from the first one whose last row sees a key of the split's tiles
+  const int tps = sg.split_keys / 64;
+  const int kvh = ref.local / sg.head_blocks;
+  int split = 0, rb = 0;
+  {
+    int j = ref.local - kvh * sg.head_blocks;
+    for (; split < sg.splits; ++split) {
+      const int X = 64 * split * tps - P;
+      const int rb0 = X > 0 ? (g * X) / (64 * RT) : 0;
+      if (j < sg.row_blocks - rb0) {
+        rb = rb0 + j;
+        break;
+      }
+      j -= sg.row_blocks - rb0;
+    }
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -180,20 +193,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
 
   const int wg_row0 = rb * 64 * RT;
   const int wg_last = min(R - 1, wg_row0 + 64 * RT - 1);
-  // 64-key tiles [64T, 64T+64); a split is a run of split_keys / 64 of them.
-  // With new_tile0 >= 0 the last split is every tile from new_tile0 = P / 64
-  // on (every tile, when it is the only split): those from new_tile0 on go
-  // through the epilogue, which reads keys at or past P from the call's rows
-  // and appends them. The other tiles come from the store through the staged
-  // loop.
+  // 64-key tiles [64T, 64T+64); a split is a run of tps of them. With
+  // new_tile0 >= 0 the tiles from new_tile0 = P / 64 on go through the
+  // epilogue, which reads keys at or past P from the call's rows; the others
+  // come from the store through the staged loop.
   const int nt0 = sg.new_tile0;
   const bool fused = nt0 >= 0;
-  const int tps = sg.split_keys / 64;
   const int t_rows = (P + wg_last / g) / 64 + 1;  // tiles any row of the block sees
-  const bool last_new = fused && split == sg.splits - 1;
-  const int t_begin = last_new ? (sg.splits == 1 ? 0 : nt0) : split * tps;
-  const int t_end = last_new ? t_rows : min(min(t_begin + tps, t_rows), fused ? nt0 : INT_MAX);
-  if (t_begin >= t_end) return;  // no row of this block sees this split
+  const int t_begin = split * tps;
+  const int t_end = min(t_begin + tps, t_rows);
+  if (t_begin >= t_end) return;  // (not launched: no row of the block sees the split)
   const int wg_min_lim = P + wg_row0 / g;
   const int t_cend = fused ? max(t_begin, min(t_end, nt0)) : t_end;
   const int ntiles = t_cend - t_begin;  // staged loop
@@ -478,11 +487,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     // 1's V part (overwriting the store's values at or past P in the piece
     // holding P). Reads past row m-1 of the call return zeros. The requests
     // of round r+1 go out once round r's V rows are transposed, so they
-    // overlap round r's products. After the rounds, the workgroups of the
-    // first row blocks (the ones with the fewest new tiles) copy the call's
-    // rows into the store (positions P .. P+m-1), 64-key tiles dealt out
-    // among them; no other workgroup of the call reads those positions
-    // except as masked keys.
+    // overlap round r's products. No workgroup of the call reads the store
+    // at positions P .. P+m-1 except as masked keys.
     const int Hkv = prm.Hkv;
     const int new_bytes = ((m - 1) * Hkv + 1) * D * 2;
     const __amdgpu_buffer_rsrc_t nkrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -568,13 +574,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       __syncthreads();
     }
 
-    // Append: workgroup rb < A takes the 64-key tiles T0 + rb, T0 + rb + A,
-    // ... of the new range. K rows are copied as they are; V rows go into
+    // Append (unsplit pieces; a split piece's rows are appended by the
+    // combine kernel): workgroup rb < A takes the 64-key tiles T0 + rb,
+    // T0 + rb + A, ... of the new range. K rows are copied as they are; V rows go into
     // LDS as [key][D + 2] (odd dword stride: the column reads below meet
     // distinct banks) and leave as 16-byte pieces of 8 keys of one column,
     // key by key in the pieces holding P or P+m.
     const int A = min(sg.row_blocks, kAppendBlocks);
-    if (rb < A) {
+    if (sg.splits == 1 && rb < A) {
       constexpr int VST = D + 2;
       uint16_t* Va = &lds[0][0][0][0];  // [64][VST]
       const uint16_t* nkh = sg.nk + (size_t)kvh * D;
@@ -1226,10 +1233,66 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
 // t+2P, ... (P = 256/D), loading BATCH of them per round, and the parts are
 // then merged in part order through lane shuffles. Every (row, head) is
 // merged in the same fixed order whatever the launch shape.
+//
+// The first append_total workgroups instead append the new rows of split
+// MFMA-path pieces to the store, D/32 per (KV head, 64-key tile of [P, P+m))
+// (the attention kernel read them from the call's inputs, and no later work
+// reads the store before this kernel ends). K rows are copied as they are;
+// V columns are gathered 8 keys at a time with lanes along d (each of a
+// wave's 8 loads reads 128 contiguous bytes) and leave as 16-byte Vt
+// pieces, key by key in the pieces holding P or P+m.
+template <int D>
+__device__ void append_new_rows(const AttnParams& p, int a) {
+  constexpr int CPR = D / 8, PARTS = D / 32;  // a tile's work in PARTS blocks
+  int s = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxSeg; ++j)
+    if (j < p.nseg && p.seg[j].append_blocks > 0 && a >= p.seg[j].append_begin) s = j;
+  const AttnSeg& sg = p.seg[s];
+  a -= sg.append_begin;
+  const int P = sg.P, m = sg.m, Hkv = p.Hkv, cap = p.cap;
+  const int T0 = P / 64, nT = (P + m - 1) / 64 - T0 + 1;
+  const int part = a % PARTS, tile = a / PARTS;
+  const int kvh = tile / nT, k0 = 64 * (T0 + tile % nT);
+  uint16_t* K = const_cast<uint16_t*>(sg.K) + (size_t)kvh * cap * D;
+  uint16_t* Vt = const_cast<uint16_t*>(sg.Vt) + (size_t)kvh * D * cap;
+  const uint16_t* nk = sg.nk + (size_t)kvh * D;
+  const uint16_t* nv = sg.nv + (size_t)kvh * D;
+  // one K piece and one 8-key V column piece per thread; every load first
+  // and unconditionally (rows clamped into [P, P+m)), so all are in flight
+  // together
+  auto row = [&](int k) { return (size_t)(min(max(k, P), P + m - 1) - P) * Hkv * D; };
+  const int it = threadIdx.x + 256 * part;
+  const int kk = k0 + it / CPR, kc = it % CPR;
+  const u32x4 kr = load16(nk + row(kk) + kc * 8);
+  const int d = it % D, k8 = k0 + 8 * (it / D);
+  uint32_t x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = nv[row(k8 + e) + d];
+  if (kk >= P && kk < P + m) store16(K + (size_t)kk * D + kc * 8, kr);
+  if (k8 + 8 <= P || k8 >= P + m) return;
+  uint16_t* dst = Vt + (size_t)d * cap + k8;
+  if (k8 >= P && k8 + 8 <= P + m) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = x[2 * e] | (x[2 * e + 1] << 16);
+    store16(dst, w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k8 + e >= P && k8 + e < P + m) dst[e] = (uint16_t)x[e];
+  }
+}
+
 template <int D, int BATCH, bool ONE>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   constexpr int CH = D / 4, PARTS = 64 / CH;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (grow, h): one per wave
+  if ((int)blockIdx.x < p.append_total) {
+    append_new_rows<D>(p, blockIdx.x);
+    return;
+  }
+  // (grow, h): one per wave
+  const int row = ((int)blockIdx.x - p.append_total) * 4 + (threadIdx.x >> 6);
   if (row >= p.total_rows * p.Hq) return;
   const int grow = row / p.Hq, h = row % p.Hq;
   int s = 0;
@@ -1255,18 +1318,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   float M = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int b0 = 0; b0 * PARTS < nvalid; b0 += BATCH) {
-    f32x4 ml[BATCH];
+    float ml[BATCH][3];  // (max, sum, scale); the fourth word is not read
     u32x2 o[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const size_t q = (size_t)min((b0 + u) * PARTS + part, nvalid - 1);
-      ml[u] = *reinterpret_cast<const f32x4*>(mlp + q * ml_stride);
+#pragma unroll
+      for (int e = 0; e < 3; ++e) ml[u][e] = mlp[q * ml_stride + e];
       o[u] = *reinterpret_cast<const u32x2*>(op + q * o_stride);
     }
+    // branch-free: a split past nvalid re-read the last valid one (finite
+    // values) and weighs 0, so every load above is issued before any use
     float Mb = M;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
-      if ((b0 + u) * PARTS + part < nvalid) Mb = fmaxf(Mb, ml[u][0]);
+      Mb = (b0 + u) * PARTS + part < nvalid ? fmaxf(Mb, ml[u][0]) : Mb;
     const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
     l *= r;
 #pragma unroll
@@ -1274,16 +1340,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     M = Mb;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      if ((b0 + u) * PARTS + part < nvalid) {
-        const float sc = fast_exp2(ml[u][0] - M);
-        const float wl = sc * ml[u][1];
-        const float wo = wl * ml[u][2];
-        l += wl;
-        acc[0] += wo * f16_bits_to_f32(o[u][0] & 0xFFFFu);
-        acc[1] += wo * f16_bits_to_f32(o[u][0] >> 16);
-        acc[2] += wo * f16_bits_to_f32(o[u][1] & 0xFFFFu);
-        acc[3] += wo * f16_bits_to_f32(o[u][1] >> 16);
-      }
+      const bool ok = (b0 + u) * PARTS + part < nvalid;
+      const float sc = fast_exp2(ml[u][0] - M);
+      const float wl = ok ? sc * ml[u][1] : 0.f;
+      const float wo = ok ? wl * ml[u][2] : 0.f;
+      l += wl;
+      acc[0] += wo * f16_bits_to_f32(o[u][0] & 0xFFFFu);
+      acc[1] += wo * f16_bits_to_f32(o[u][0] >> 16);
+      acc[2] += wo * f16_bits_to_f32(o[u][1] & 0xFFFFu);
+      acc[3] += wo * f16_bits_to_f32(o[u][1] >> 16);
     }
   }
   // merge the parts in order: part 0 absorbs parts 1 .. PARTS-1 (always
@@ -1364,7 +1429,7 @@ static void launch_mfma(const AttnParams& p, hipStream_t st) {
 
 template <int D, bool ONE>
 static void launch_combine(const AttnParams& p, bool wide, hipStream_t st) {
-  const int blocks = (p.total_rows * p.Hq + 3) / 4;
+  const int blocks = p.append_total + (p.total_rows * p.Hq + 3) / 4;
   if (wide)
     hipLaunchKernelGGL((attn_combine_kernel<D, 16, ONE>), dim3(blocks), dim3(256), 0, st, p);
   else

@@ -39,13 +39,18 @@ struct AttnSeg {
   int row_blocks;      // per KV head
   int splits, split_keys;
   int tail_split;      // decode layout: splits-1 cached splits of split_keys, then [P, P+m)
+  // MFMA path: split s holds the 64-key tiles [s, s+1) * split_keys / 64,
+  // and a row block has a workgroup for split s only when one of its rows
+  // sees a key there; head_blocks workgroups per KV head, split-major.
+  int head_blocks;
   // MFMA path: first 64-key tile [64t, 64t+64) that holds new keys (P / 64).
-  // With new_tile0 >= 0 the piece's splits-1 first splits hold split_keys
-  // cached keys each (below 64 * new_tile0) and the last split every tile
-  // from new_tile0 on, whose keys at or past P the attention kernel reads
-  // from nk/nv and appends itself. -1: every key is in the store, appended
-  // beforehand, and the splits cut [0, P+m) evenly.
+  // With new_tile0 >= 0 the attention kernel reads keys at or past P from
+  // nk/nv (tiles from new_tile0 on); the rows are appended by the combine
+  // kernel's first append_blocks workgroups (D / 32 per KV head and 64-key
+  // tile of [P, P+m)), or, for an unsplit piece (append_blocks 0), by the
+  // attention kernel. -1: every key is in the store, appended beforehand.
   int new_tile0;
+  int append_blocks, append_begin;
   int block_begin;     // first linear workgroup of this piece
   int row_begin;       // first output row of this piece in a combined launch
 };
@@ -56,6 +61,7 @@ struct AttnParams {
   int Hq, Hkv, g, D, cap;
   int total_blocks;
   int total_rows;      // sum of m over pieces
+  int append_total;    // combine-kernel append workgroups (before the combine's own)
   float c;             // log2(e) / sqrt(D)
   int dec_rt, dec_ns;  // decode path: 16-row tiles per block (1, 2), steps per round (1, 2)
   int total_rows_hint; // rows of the whole call (planning only)

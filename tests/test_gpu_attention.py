@@ -331,6 +331,38 @@ def test_batched_matches_single_slot_calls():
         row += ms[i]
 
 
+def test_batched_split_and_unsplit_pieces_append():
+    """One MFMA launch with an unsplit piece (no cached keys, one 64-key
+    tile: the attention kernel appends its rows) beside split pieces (the
+    combine kernel appends theirs): every piece matches the oracle and every
+    appended row is in the store, bit for bit."""
+    hq, hkv, d = 32, 8, 128
+    Ps, ms = [0, 500, 130], [60, 30, 100]
+    st = sve.KVSlots(3, 1, hq, hkv, d, 1024, 1024)
+    cases = [synth.attention_case(60 + i, hq, hkv, d, Ps[i], ms[i]) for i in range(3)]
+    announce("batched split and unsplit pieces")
+    for i in range(3):
+        toks = np.concatenate([[i + 1], np.arange(Ps[i] + ms[i] - 1)]).astype(np.int32)
+        slot, r = st.kv_slot_select(toks)
+        assert (slot, r) == (i, 0)
+        if Ps[i]:
+            st.extend_attn(slot, 0, dev_bf16(cases[i]["q_prefix"]),
+                           dev_bf16(cases[i]["k_prefix"]), dev_bf16(cases[i]["v_prefix"]))
+    q = dev_bf16(np.concatenate([c["q"] for c in cases]))
+    k = dev_bf16(np.concatenate([c["k"] for c in cases]))
+    v = dev_bf16(np.concatenate([c["v"] for c in cases]))
+    out = host_f64_of_bf16(st.extend_attn_batched([0, 1, 2], ms, 0, q, k, v))
+    row = 0
+    for i, c in enumerate(cases):
+        kc = np.concatenate([c["k_prefix"], c["k"]])
+        vc = np.concatenate([c["v_prefix"], c["v"]])
+        want = extend_attention(c["q"], kc, vc, Ps[i])
+        assert np.abs(out[row:row + ms[i]] - want).max() <= ATTN_TOL
+        kk, vv = st.kv_read(i, 0, 0, Ps[i] + ms[i])
+        assert np.array_equal(host_bits(kk), kc) and np.array_equal(host_bits(vv), vc)
+        row += ms[i]
+
+
 def test_kernel_timing_records_each_call():
     """Timing events around the three kernels of each timed call: positive
     attention time, a count capped at the requested calls, state errors,
