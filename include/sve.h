@@ -173,6 +173,23 @@ int sve_w4_dequant(const void* packed, int32_t N, int32_t K, float* out, void* h
 int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
                   void* hip_stream);
 
+/* Many-row int4 GEMM for a prefill's new rows ([goinfer] "The problem": a
+ * prefill runs every new prompt token through each weight matrix, so a turn
+ * of m new tokens is an m-row product per matrix; [quant] "Quantizations":
+ * the group-32 blocks are used in place). Same result definition as
+ * sve_w4_gemv_m, for any number of rows: y[r][n] = sum_k x[r][k] * w[n][k],
+ * w = (code - 8) * scale, accumulated in fp32.
+ *   x: device bf16 [m][K]; packed: sve_w4_pack output; y: device fp32 [m][N];
+ *   workspace: device memory of at least sve_w4_gemm_workspace_bytes(m, N,
+ *   K) bytes (may be NULL when that is 0), owned by the caller and used
+ *   only during the call's kernels (k-split partial results).
+ *   m >= 1, N >= 1, K % 32 == 0. The result depends only on (x, w, m, N, K):
+ *   repeated calls give identical bits.
+ * Errors: SVE_E_ARG (shape, null pointer, workspace too small), SVE_E_HIP. */
+size_t sve_w4_gemm_workspace_bytes(int32_t m, int32_t N, int32_t K);
+int sve_w4_gemm(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
+                void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Expert-routed GEMV for a mixture-of-experts layer ([spec] "Architecture
  * decides whether it pays": rows pick different experts, so expert weights
  * are not shared across rows). Pair (r, j) computes

@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import SveError, check
 
-__all__ = ["KVSlots", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m",
+__all__ = ["KVSlots", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m", "w4_gemm",
+           "w4_gemm_workspace_bytes",
            "w4_gemv_m_routed", "verify_workspace_bytes", "verify_accept", "SpecGate",
            "spec_break_even", "probe_read", "probe_copy", "SveError", "load_library"]
 
@@ -197,6 +198,32 @@ def w4_gemv_m(x: torch.Tensor, packed: torch.Tensor, n: int, k: int,
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _need(y, torch.float32, (m, n), "y")
     check(lib.sve_w4_gemv_m(_ptr(x), m, _ptr(packed), n, k, _ptr(y), _stream()))
+    return y
+
+
+def w4_gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Device workspace bytes w4_gemm needs for this shape (0: none)."""
+    return int(_lib.load().sve_w4_gemm_workspace_bytes(m, n, k))
+
+
+def w4_gemm(x: torch.Tensor, packed: torch.Tensor, n: int, k: int,
+            y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y [m][N] fp32 = x [m][K] bf16 times the packed int4 weight, any m."""
+    lib = _lib.load()
+    m = x.shape[0]
+    _need(x, torch.bfloat16, (m, k), "x")
+    _need(packed, torch.uint8, (lib.sve_w4_packed_bytes(n, k),), "packed")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, (m, n), "y")
+    ws_bytes = lib.sve_w4_gemm_workspace_bytes(m, n, k)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _need(workspace, torch.uint8, None, "workspace")
+    check(lib.sve_w4_gemm(_ptr(x), m, _ptr(packed), n, k, _ptr(y),
+                          _ptr(workspace) if workspace is not None else None,
+                          workspace.numel() if workspace is not None else 0, _stream()))
     return y
 
 

@@ -665,6 +665,24 @@ int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32
   return SVE_OK;
 }
 
+size_t sve_w4_gemm_workspace_bytes(int32_t m, int32_t N, int32_t K) {
+  if (m < 1 || N < 1 || K < 32 || K % 32) return 0;
+  return w4_gemm_workspace_bytes(m, N, K);
+}
+
+int sve_w4_gemm(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
+                void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (m < 1 || N < 1 || K < 32 || K % 32)
+    return fail(nullptr, SVE_E_ARG, "need m >= 1, N >= 1 and K % 32 == 0");
+  if ((long long)m * N > (1LL << 40) / 4) return fail(nullptr, SVE_E_ARG, "m * N too large");
+  if (!x || !packed || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
+  const size_t need = w4_gemm_workspace_bytes(m, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(nullptr, SVE_E_ARG, "workspace smaller than sve_w4_gemm_workspace_bytes");
+  SVE_HIP(nullptr, launch_w4_gemm(x, m, packed, N, K, y, workspace, (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
 int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int32_t* ids,
                          int32_t topk, const void* packed_all, int32_t E, int32_t N, int32_t K,
                          float* y, void* hip_stream) {

@@ -55,6 +55,20 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// Direct global-to-LDS loads (buffer_load ... lds, 16 bytes per lane)
+// through raw buffer resources: LDS pointer type and word 3 of a resource
+// (32-bit data format, no swizzle).
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kBufWord3 = 0x00020000;
+
+// wait until at most N vector-memory requests of this wave are outstanding
+// (lgkm and export counters untouched)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __device__ __forceinline__ float xor_shfl(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }

@@ -128,10 +128,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
 // and its Vt A operand is one 16-byte LDS read. Each lane owns one packed
 // row (lane % 16): row statistics need two cross-lane steps only.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-// word 3 of a raw buffer resource (32-bit data format, no swizzle)
-constexpr int kBufWord3 = 0x00020000;
-
 // swizzled 16-byte chunk position of chunk c in K-tile row `key` (D/8 chunks
 // per row) and in Vt-tile row `d` (8 chunks per row)
 template <int D>
@@ -140,14 +136,6 @@ __device__ __forceinline__ int kswz(int key, int c) {
   return c ^ (((key & (CPR - 1)) ^ (((key >> 4) & 1) << 2)) & (CPR - 1));
 }
 __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
-
-// wait until at most N vector-memory requests of this wave are outstanding
-// (lgkm and export counters untouched)
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // ONE: the call has a single piece (its fields load without first finding
 // the piece, one scalar round trip less)

@@ -812,6 +812,229 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
 // host launchers
 // ---------------------------------------------------------------------------
 
+// ---------------------------------------------------------------------------
+// int4 GEMM for many rows (a prefill's m >= 16): y = x W^T with the same
+// exact arithmetic as the GEMV (B = bf16(128 + code), C0 = -136 * sum x per
+// group through one more product, the fp16 group scale applied in fp32).
+// Workgroup = four waves over one 64-column tile and 256 rows; wave = 64
+// rows x 64 columns (4 x 4 tiles of 16 x 16).
+//   weights: a ring of four LDS slots (quads), shared by the four waves;
+//     each wave loads one 16-row tile's nibble and scale blocks per quad by
+//     direct buffer-to-LDS loads, three quads ahead (the first touch comes
+//     from HBM). Each slot is its own LDS variable and the quad loop is
+//     unrolled by four, so every access names its slot: the compiler then
+//     waits, before reading a slot, only for the loads into that slot.
+//   activations: the wave's own rows, 16-byte A operands straight into
+//     registers, two groups ahead.
+// The weight loads are waited for explicitly (a constant count of requests
+// issued since) and published to the other waves by a barrier per quad. The
+// k range may be split over several workgroups (grid z); each split then
+// writes its partial y to a workspace, and a second kernel adds the splits
+// in split order.
+// ---------------------------------------------------------------------------
+constexpr int kGemmWaveRows = 64;
+constexpr int kGemmCols = 64;
+constexpr int kGemmGroupRows = 4 * kGemmWaveRows;
+constexpr int kGemmMaxSplits = 16;
+constexpr int kGemmWAhead = 3;  // weight quads requested ahead (ring of 4)
+constexpr int kGemmXAhead = 2;  // activation groups requested ahead
+
+struct GemmWSlot {
+  uint8_t nib[4][1024];  // [tile][64 lanes x 16 bytes]
+  uint8_t scl[4][128];   // [tile][16 rows x 8 bytes]
+};
+
+__global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restrict__ x, int m,
+                                                         const uint8_t* __restrict__ nib,
+                                                         const uint8_t* __restrict__ scl, int N,
+                                                         int K, int Q, int qps,
+                                                         float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) GemmWSlot ws0, ws1, ws2, ws3;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, r = lane & 15;
+  const int m0 = blockIdx.y * kGemmGroupRows + wave * kGemmWaveRows;
+  const bool live = m0 < m;  // (uniform) rows of this wave exist; it loads either way
+  const int n_tiles = (N + 15) / 16, G = K >> 5;
+  const int q0 = blockIdx.z * qps, q1 = min(Q, q0 + qps);
+  const bf16x8 neg136 = neg136_operand();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // this wave's weight tile, the weight buffer resources
+  const int tw = min(4 * (int)blockIdx.x + wave, n_tiles - 1);
+  const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(nib), (short)0, n_tiles * Q * 1024, kBufWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(scl), (short)0, n_tiles * Q * 128, kBufWord3);
+  // quad q's blocks of tile tw into a slot (two requests; past the split a
+  // real block, unused)
+  auto issue_w = [&](GemmWSlot& sl, int q) {
+    q = min(q, Q - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(nrs, (lds_void*)&sl.nib[wave][0], 16, lane * 16,
+                                             (tw * Q + q) * 1024, 0, 0);
+    if (lane < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)&sl.scl[wave][0], 16, lane * 16,
+                                               (tw * Q + q) * 128, 0, 0);
+  };
+  auto slot = [&](int u) -> GemmWSlot& { return u == 0 ? ws0 : u == 1 ? ws1 : u == 2 ? ws2 : ws3; };
+
+  // A operands of group g for the wave's four 16-row tiles (rows past m
+  // repeat row m-1; groups past K read a real group, whose weights are code
+  // 8 with scale 0) - four requests
+  const uint16_t* xr[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) xr[a] = x + (size_t)min(m0 + 16 * a + r, m - 1) * K + 8 * kb;
+  auto load_x = [&](int g, bf16x8* xa) {
+    g = min(g, G - 1);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) xa[a] = as_bf16x8(load16(xr[a] + 32 * g));
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[a][t] = zero4;
+
+  // prologue: weight quads q0 .. q0+2 into slots 0..2, groups 4q0, 4q0+1
+  issue_w(ws0, q0);
+  issue_w(ws1, q0 + 1);
+  issue_w(ws2, q0 + 2);
+  bf16x8 x1[4], x2[4];
+  load_x(4 * q0, x1);
+  load_x(4 * q0 + 1, x2);
+  wait_vmem<8>();  // the three weight quads are in
+
+  for (int qb = q0; qb < q1; qb += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = qb + u;
+      if (q >= q1) break;
+      // weight quad q (slot u) is in for this wave: since it was requested,
+      // 16 activation and 2 weight requests per later quad; the barrier
+      // publishes every wave's part and frees slot (u+3)%4 (quad q-1)
+      // (a bare s_barrier: a fenced one would also wait for the quads still
+      // in flight, which are LDS writes)
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmem<16 * kGemmWAhead + 2 * (kGemmWAhead - 1)>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(slot((u + 3) & 3), q + kGemmWAhead);
+      u32x4 wq[4];
+      u32x2 sq[4];
+      GemmWSlot& cur = slot(u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        wq[t] = *reinterpret_cast<const u32x4*>(&cur.nib[t][lane * 16]);
+        sq[t] = *reinterpret_cast<const u32x2*>(&cur.scl[t][r * 8]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 xa[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          xa[a] = x1[a];
+          x1[a] = x2[a];
+        }
+        load_x(4 * q + j + kGemmXAhead, x2);
+        if (!live) continue;
+        f32x4 c0[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) c0[a] = mfma16x16x32(xa[a], neg136, zero4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 bf = w4_bfrag(wq[t][j]);
+          const float s = scale_of(sq[t], j);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 d = mfma16x16x32(xa[a], bf, c0[a]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][t][i] = fmaf(s, d[i], acc[a][t][i]);
+          }
+        }
+        // products of a tile, then the scaled adds of the tile before
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      }
+    }
+  }
+  wait_vmem<0>();  // no request may land in LDS after the workgroup ends
+  if (!live) return;
+
+  // lane holds rows m0 + 16a + 4kb + i of column 64 * tile + 16t + r
+  float* o = out + (size_t)blockIdx.z * m * N;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int col = kGemmCols * blockIdx.x + 16 * t + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * a + 4 * kb + i;
+        if (row < m && col < N) o[(size_t)row * N + col] = acc[a][t][i];
+      }
+    }
+}
+
+// y = sum of the splits' partial results, in split order
+__global__ __launch_bounds__(256) void w4_gemm_reduce_kernel(const float* __restrict__ ws, int ks,
+                                                             long long mn, float* __restrict__ y) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float s = ws[i];
+  for (int k = 1; k < ks; ++k) s += ws[(size_t)k * mn + i];
+  y[i] = s;
+}
+
+// k splits of the GEMM: enough workgroups for two per compute unit, at most
+// kGemmMaxSplits and at most one per quad of 128 k
+int w4_gemm_splits(int m, int N, int K) {
+  const int Q = (K + 127) / 128;
+  const int base = ((N + kGemmCols - 1) / kGemmCols) * ((m + kGemmGroupRows - 1) / kGemmGroupRows);
+  int ks = std::max(1, std::min({512 / std::max(base, 1), kGemmMaxSplits, Q}));
+  const int forced = getenv("SVE_GEMM_SPLITS") ? atoi(getenv("SVE_GEMM_SPLITS")) : 0;
+  if (forced > 0) ks = std::min({forced, kGemmMaxSplits, Q});
+  const int qps = (Q + ks - 1) / ks;
+  return (Q + qps - 1) / qps;
+}
+
+size_t w4_gemm_workspace_bytes(int m, int N, int K) {
+  const int ks = w4_gemm_splits(m, N, K);
+  return ks > 1 ? (size_t)ks * m * N * sizeof(float) : 0;
+}
+
+hipError_t launch_w4_gemm(const void* x, int m, const void* packed, int N, int K, float* y,
+                          void* ws, hipStream_t st) {
+  const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
+  const uint8_t* nib = (const uint8_t*)packed;
+  const uint8_t* scl = nib + (size_t)n_tiles * Q * 1024;
+  const int ks = w4_gemm_splits(m, N, K);
+  const int qps = (Q + ks - 1) / ks;
+  // the kernel's buffer offsets are 32-bit
+  if ((size_t)n_tiles * Q * 1024 >= (1u << 31) || (size_t)m * K * 2 >= (1u << 31))
+    return hipErrorInvalidValue;
+  const dim3 grid((N + kGemmCols - 1) / kGemmCols, (m + kGemmGroupRows - 1) / kGemmGroupRows, ks);
+  float* out = ks > 1 ? (float*)ws : y;
+  hipLaunchKernelGGL(w4_gemm_kernel, grid, dim3(256), 0, st, (const uint16_t*)x, m, nib,
+                     scl, N, K, Q, qps, out);
+  if (ks > 1) {
+    const long long mn = (long long)m * N;
+    hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
+                       (const float*)ws, ks, mn, y);
+  }
+  return hipGetLastError();
+}
+
 static int env_int_w4(const char* name, int dflt) {
   const char* v = getenv(name);
   return (v && *v) ? atoi(v) : dflt;

@@ -13,6 +13,12 @@ hipError_t launch_w4_pack(const uint8_t* w, const uint16_t* s, int N, int K, voi
 hipError_t launch_w4_dequant(const void* packed, int N, int K, float* out, hipStream_t st);
 hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K, float* y,
                           hipStream_t st, int wgs_per_cu);
+// many-row GEMM: workspace of w4_gemm_workspace_bytes(m, N, K) bytes (0:
+// unused) for the k splits' partial results
+int w4_gemm_splits(int m, int N, int K);
+size_t w4_gemm_workspace_bytes(int m, int N, int K);
+hipError_t launch_w4_gemm(const void* x, int m, const void* packed, int N, int K, float* y,
+                          void* ws, hipStream_t st);
 hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int32_t* ids,
                                  int topk, const void* packed_all, int E, int N, int K, float* y,
                                  hipStream_t st);

@@ -73,6 +73,18 @@ def test_w4_argument_checks(lib):
     assert lib.sve_w4_gemv_m_routed(p, 2, 1, p, 1, p, 4, 16, 128, p, None) == _lib.SVE_E_ARG
     assert lib.sve_w4_pack(p, p, 0, 128, p, None) == _lib.SVE_E_ARG
     assert lib.sve_w4_dequant(p, 16, 31, p, None) == _lib.SVE_E_ARG
+    # many-row GEMM: shape and pointer checks, and a workspace no smaller
+    # than what the plan needs (all before anything is enqueued)
+    assert lib.sve_w4_gemm_workspace_bytes(0, 16, 128) == 0
+    assert lib.sve_w4_gemm_workspace_bytes(16, 16, 100) == 0
+    assert lib.sve_w4_gemm(p, 0, p, 16, 128, p, None, 0, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemm(p, 20, p, 0, 128, p, None, 0, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemm(p, 20, p, 16, 96 + 1, p, None, 0, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemm(None, 20, p, 16, 128, p, None, 0, None) == _lib.SVE_E_ARG
+    need = lib.sve_w4_gemm_workspace_bytes(254, 4608, 3584)
+    assert need > 0  # a k-split plan for a few-column matrix
+    assert lib.sve_w4_gemm(p, 254, p, 4608, 3584, p, None, 0, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemm(p, 254, p, 4608, 3584, p, p, need - 1, None) == _lib.SVE_E_ARG
 
 
 def test_null_context_is_rejected(lib):
