@@ -178,11 +178,14 @@ int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32
  * of m new tokens is an m-row product per matrix; [quant] "Quantizations":
  * the group-32 blocks are used in place). Same result definition as
  * sve_w4_gemv_m, for any number of rows: y[r][n] = sum_k x[r][k] * w[n][k],
- * w = (code - 8) * scale, accumulated in fp32.
+ * w = (code - 8) * scale. It multiplies fp16 operands and accumulates in
+ * fp32: each weight is (code - 8) * scale rounded once to fp16 (relative
+ * error at most 2^-11) and x is converted to fp16 (exact for |x| < 65504;
+ * larger values become infinite).
  *   x: device bf16 [m][K]; packed: sve_w4_pack output; y: device fp32 [m][N];
  *   workspace: device memory of at least sve_w4_gemm_workspace_bytes(m, N,
- *   K) bytes (may be NULL when that is 0), owned by the caller and used
- *   only during the call's kernels (k-split partial results).
+ *   K) bytes, owned by the caller and used only during the call's kernels
+ *   (x in fp16, and k-split partial results).
  *   m >= 1, N >= 1, K % 32 == 0. The result depends only on (x, w, m, N, K):
  *   repeated calls give identical bits.
  * Errors: SVE_E_ARG (shape, null pointer, workspace too small), SVE_E_HIP. */

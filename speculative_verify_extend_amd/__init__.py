@@ -216,14 +216,12 @@ def w4_gemm(x: torch.Tensor, packed: torch.Tensor, n: int, k: int,
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _need(y, torch.float32, (m, n), "y")
-    ws_bytes = lib.sve_w4_gemm_workspace_bytes(m, n, k)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    if workspace is not None:
-        _need(workspace, torch.uint8, None, "workspace")
-    check(lib.sve_w4_gemm(_ptr(x), m, _ptr(packed), n, k, _ptr(y),
-                          _ptr(workspace) if workspace is not None else None,
-                          workspace.numel() if workspace is not None else 0, _stream()))
+    if workspace is None:
+        workspace = torch.empty(max(lib.sve_w4_gemm_workspace_bytes(m, n, k), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, None, "workspace")
+    check(lib.sve_w4_gemm(_ptr(x), m, _ptr(packed), n, k, _ptr(y), _ptr(workspace),
+                          workspace.numel(), _stream()))
     return y
 
 

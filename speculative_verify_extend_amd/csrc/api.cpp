@@ -674,10 +674,11 @@ int sve_w4_gemm(const void* x, int32_t m, const void* packed, int32_t N, int32_t
                 void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (m < 1 || N < 1 || K < 32 || K % 32)
     return fail(nullptr, SVE_E_ARG, "need m >= 1, N >= 1 and K % 32 == 0");
-  if ((long long)m * N > (1LL << 40) / 4) return fail(nullptr, SVE_E_ARG, "m * N too large");
+  if ((long long)m * N > (1LL << 40) / 4 || (long long)m * K * 2 >= (1LL << 31))
+    return fail(nullptr, SVE_E_ARG, "m * N or m * K too large for one call");
   if (!x || !packed || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
   const size_t need = w4_gemm_workspace_bytes(m, N, K);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (!workspace || workspace_bytes < need)
     return fail(nullptr, SVE_E_ARG, "workspace smaller than sve_w4_gemm_workspace_bytes");
   SVE_HIP(nullptr, launch_w4_gemm(x, m, packed, N, K, y, workspace, (hipStream_t)hip_stream));
   return SVE_OK;

@@ -813,23 +813,27 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
 // ---------------------------------------------------------------------------
 
 // ---------------------------------------------------------------------------
-// int4 GEMM for many rows (a prefill's m >= 16): y = x W^T with the same
-// exact arithmetic as the GEMV (B = bf16(128 + code), C0 = -136 * sum x per
-// group through one more product, the fp16 group scale applied in fp32).
+// int4 GEMM for many rows (a prefill's m >= 16): y = x W^T on fp16 matrix
+// cores. Unlike the GEMV, whose group scale costs one fp32 multiply-add per
+// output and group (as many vector operations as the products themselves
+// at this size), the GEMM dequantises each weight once per workgroup to
+// fp16: w = (code - 8) * scale rounded once (relative error at most 2^-11),
+// and x is converted to fp16 once by a first pass (exact for |x| < 65504).
+// The products then accumulate in fp32 with no vector work per product.
 // Workgroup = four waves over one 64-column tile and 256 rows; wave = 64
 // rows x 64 columns (4 x 4 tiles of 16 x 16).
-//   weights: a ring of four LDS slots (quads), shared by the four waves;
-//     each wave loads one 16-row tile's nibble and scale blocks per quad by
-//     direct buffer-to-LDS loads, three quads ahead (the first touch comes
-//     from HBM). Each slot is its own LDS variable and the quad loop is
-//     unrolled by four, so every access names its slot: the compiler then
-//     waits, before reading a slot, only for the loads into that slot.
-//   activations: the wave's own rows, 16-byte A operands straight into
-//     registers, two groups ahead.
-// The weight loads are waited for explicitly (a constant count of requests
-// issued since) and published to the other waves by a barrier per quad. The
-// k range may be split over several workgroups (grid z); each split then
-// writes its partial y to a workspace, and a second kernel adds the splits
+//   weights: nibble and scale blocks reach a ring of four LDS slots by
+//     direct buffer-to-LDS loads, three quads ahead, each wave loading one
+//     16-row tile (each slot its own LDS variable and the quad loop
+//     unrolled by four, so a read waits only for its slot's loads). While
+//     the products of quad q run, each wave dequantises its tile of quad
+//     q+1 into the fp16 operand buffer of that quad's parity, which all four
+//     waves read after the next barrier (one barrier per quad).
+//   activations: the wave's own rows, packed by the first pass in operand
+//     order (each A operand a contiguous 1 KB block), straight into
+//     registers two groups ahead.
+// The k range may be split over several workgroups (grid z); each split then
+// writes its partial y to the workspace, and a second kernel adds the splits
 // in split order.
 // ---------------------------------------------------------------------------
 constexpr int kGemmWaveRows = 64;
@@ -839,17 +843,70 @@ constexpr int kGemmMaxSplits = 16;
 constexpr int kGemmWAhead = 3;  // weight quads requested ahead (ring of 4)
 constexpr int kGemmXAhead = 2;  // activation groups requested ahead
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 struct GemmWSlot {
   uint8_t nib[4][1024];  // [tile][64 lanes x 16 bytes]
   uint8_t scl[4][128];   // [tile][16 rows x 8 bytes]
 };
 
-__global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restrict__ x, int m,
+// fp16 B operand of one group from a lane's nibble dword: (code - 8) * s
+__device__ __forceinline__ u32x4 w4_f16frag(uint32_t dw, f16x2 s2) {
+  constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x64006400u;  // fp16 1024 + code
+  const f16x2 off = {(_Float16)-1032.f, (_Float16)-1032.f};
+  u32x4 b;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t v = __builtin_amdgcn_bitop3_b32(dw >> (4 * p), kMask, kExp, 0xEA);
+    f16x2 h = __builtin_bit_cast(f16x2, v) + off;  // code - 8, exact
+    h = h * s2;                                      // one rounding
+    b[p] = __builtin_bit_cast(uint32_t, h);
+  }
+  return b;
+}
+
+// x (bf16 [m][K]) to fp16 in MFMA operand order: block (row tile rt of 16
+// rows, group g) is 1 KB at (rt * G + g) * 1024 bytes, lane (r, kb) of it
+// holding row 16 rt + r, elements 32 g + 8 kb .. +7 (the A operand of one
+// product); rows from m up to a multiple of 64 are zero. One 16-byte piece
+// per thread.
+__global__ __launch_bounds__(256) void w4_x_pack_kernel(const uint16_t* __restrict__ x, int m,
+                                                        int K, long long pieces,
+                                                        uint16_t* __restrict__ xp) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int G = K >> 5;
+  const int lane = (int)(i & 63);
+  const long long blk = i >> 6;
+  const int g = (int)(blk % G), rt = (int)(blk / G);
+  const int row = 16 * rt + (lane & 15);
+  u32x4 h = {0u, 0u, 0u, 0u};
+  if (row < m) {
+    const u32x4 v = load16(x + (size_t)row * K + 32 * g + 8 * (lane >> 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f16x2 p;
+      p[0] = (_Float16)__uint_as_float(v[e] << 16);
+      p[1] = (_Float16)__uint_as_float(v[e] & 0xFFFF0000u);
+      h[e] = __builtin_bit_cast(uint32_t, p);
+    }
+  }
+  store16(xp + 8 * i, h);
+}
+
+__global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restrict__ xh, int m,
                                                          const uint8_t* __restrict__ nib,
                                                          const uint8_t* __restrict__ scl, int N,
                                                          int K, int Q, int qps,
                                                          float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) GemmWSlot ws0, ws1, ws2, ws3;
+  // fp16 B operands of a quad: [tile][group][64 lanes x 16 bytes], by parity
+  __shared__ __attribute__((aligned(16))) uint8_t bq0[4][4][1024], bq1[4][4][1024];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kb = lane >> 4, r = lane & 15;
@@ -857,7 +914,6 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
   const bool live = m0 < m;  // (uniform) rows of this wave exist; it loads either way
   const int n_tiles = (N + 15) / 16, G = K >> 5;
   const int q0 = blockIdx.z * qps, q1 = min(Q, q0 + qps);
-  const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // this wave's weight tile, the weight buffer resources
@@ -878,16 +934,18 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
   };
   auto slot = [&](int u) -> GemmWSlot& { return u == 0 ? ws0 : u == 1 ? ws1 : u == 2 ? ws2 : ws3; };
 
-  // A operands of group g for the wave's four 16-row tiles (rows past m
-  // repeat row m-1; groups past K read a real group, whose weights are code
-  // 8 with scale 0) - four requests
-  const uint16_t* xr[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) xr[a] = x + (size_t)min(m0 + 16 * a + r, m - 1) * K + 8 * kb;
-  auto load_x = [&](int g, bf16x8* xa) {
+  // A operands of group g for the wave's four 16-row tiles: four 1 KB
+  // blocks of the packed x (rows past m are zero; groups past K read a real
+  // group, whose weights are code 8 with scale 0) - four requests
+  // (a wave with no rows loads the first wave's blocks, unused: its loads
+  // keep the request counts the same)
+  const uint8_t* xw = reinterpret_cast<const uint8_t*>(xh) +
+                      (size_t)((live ? m0 : 0) / 16) * G * 1024 + lane * 16;
+  auto load_x = [&](int g, f16x8* xa) {
     g = min(g, G - 1);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) xa[a] = as_bf16x8(load16(xr[a] + 32 * g));
+    for (int a = 0; a < 4; ++a)
+      xa[a] = __builtin_bit_cast(f16x8, load16(xw + ((size_t)a * G + g) * 1024));
   };
 
   f32x4 acc[4][4];
@@ -896,42 +954,56 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[a][t] = zero4;
 
-  // prologue: weight quads q0 .. q0+2 into slots 0..2, groups 4q0, 4q0+1
+  // dequantise this wave's tile of the quad in slot sl into operand buffer bq
+  auto dequant = [&](GemmWSlot& sl, uint8_t (*bq)[4][1024]) {
+    const u32x4 wd = *reinterpret_cast<const u32x4*>(&sl.nib[wave][lane * 16]);
+    const u32x2 sv = *reinterpret_cast<const u32x2*>(&sl.scl[wave][r * 8]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sw = sv[j >> 1] >> (16 * (j & 1));
+      const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
+      const f16x2 s2 = {s, s};
+      *reinterpret_cast<u32x4*>(&bq[wave][j][lane * 16]) = w4_f16frag(wd[j], s2);
+    }
+  };
+
+  // prologue: weight quads q0 .. q0+2 into slots 0..2 and groups 4q0, 4q0+1
+  // requested; quad q0 dequantised into operand buffer 0
   issue_w(ws0, q0);
   issue_w(ws1, q0 + 1);
   issue_w(ws2, q0 + 2);
-  bf16x8 x1[4], x2[4];
+  f16x8 x1[4], x2[4];
   load_x(4 * q0, x1);
   load_x(4 * q0 + 1, x2);
   wait_vmem<8>();  // the three weight quads are in
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  dequant(ws0, bq0);
 
+  // Quad q: one barrier (every wave has finished quad q-1 and written the
+  // operands of quad q; the weight blocks of quad q+1 are in); then the
+  // products of quad q run beside the dequantisation of quad q+1 into the
+  // other operand buffer (last read in quad q-1).
   for (int qb = q0; qb < q1; qb += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = qb + u;
       if (q >= q1) break;
-      // weight quad q (slot u) is in for this wave: since it was requested,
-      // 16 activation and 2 weight requests per later quad; the barrier
-      // publishes every wave's part and frees slot (u+3)%4 (quad q-1)
-      // (a bare s_barrier: a fenced one would also wait for the quads still
-      // in flight, which are LDS writes)
+      // weight quad q+1 (slot (u+1)%4, requested at the start of quad q-2)
+      // is in for this wave: since then 16 activation requests per quad
+      // and one weight pair. A bare s_barrier: a fenced one would also wait
+      // for the quads still in flight, which are LDS writes.
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmem<16 * kGemmWAhead + 2 * (kGemmWAhead - 1)>();
+      wait_vmem<32 + 2>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       issue_w(slot((u + 3) & 3), q + kGemmWAhead);
-      u32x4 wq[4];
-      u32x2 sq[4];
-      GemmWSlot& cur = slot(u);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wq[t] = *reinterpret_cast<const u32x4*>(&cur.nib[t][lane * 16]);
-        sq[t] = *reinterpret_cast<const u32x2*>(&cur.scl[t][r * 8]);
-      }
+      uint8_t(*bq)[4][1024] = (u & 1) ? bq1 : bq0;
+      uint8_t(*bn)[4][1024] = (u & 1) ? bq0 : bq1;
+      dequant(slot((u + 1) & 3), bn);  // quad q+1 (past the split: unused)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 xa[4];
+        f16x8 xa[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           xa[a] = x1[a];
@@ -939,32 +1011,14 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
         }
         load_x(4 * q + j + kGemmXAhead, x2);
         if (!live) continue;
-        f32x4 c0[4];
+        f16x8 bf[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) c0[a] = mfma16x16x32(xa[a], neg136, zero4);
+        for (int t = 0; t < 4; ++t)
+          bf[t] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&bq[t][j][lane * 16]));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 bf = w4_bfrag(wq[t][j]);
-          const float s = scale_of(sq[t], j);
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const f32x4 d = mfma16x16x32(xa[a], bf, c0[a]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[a][t][i] = fmaf(s, d[i], acc[a][t][i]);
-          }
-        }
-        // products of a tile, then the scaled adds of the tile before
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-#pragma unroll
-        for (int t = 1; t < 4; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+          for (int a = 0; a < 4; ++a) acc[a][t] = mfma16x16x32_f16(xa[a], bf[t], acc[a][t]);
       }
     }
   }
@@ -1008,9 +1062,15 @@ int w4_gemm_splits(int m, int N, int K) {
   return (Q + qps - 1) / qps;
 }
 
+// workspace: x in fp16 in operand order (rows padded to a multiple of 64),
+// then the splits' partial results ([splits][m][N] fp32) when k is split
+static size_t gemm_xh_bytes(int m, int K) {
+  return (size_t)((m + kGemmWaveRows - 1) / kGemmWaveRows) * kGemmWaveRows * K * 2;
+}
+
 size_t w4_gemm_workspace_bytes(int m, int N, int K) {
   const int ks = w4_gemm_splits(m, N, K);
-  return ks > 1 ? (size_t)ks * m * N * sizeof(float) : 0;
+  return gemm_xh_bytes(m, K) + (ks > 1 ? (size_t)ks * m * N * sizeof(float) : 0);
 }
 
 hipError_t launch_w4_gemm(const void* x, int m, const void* packed, int N, int K, float* y,
@@ -1024,13 +1084,17 @@ hipError_t launch_w4_gemm(const void* x, int m, const void* packed, int N, int K
   if ((size_t)n_tiles * Q * 1024 >= (1u << 31) || (size_t)m * K * 2 >= (1u << 31))
     return hipErrorInvalidValue;
   const dim3 grid((N + kGemmCols - 1) / kGemmCols, (m + kGemmGroupRows - 1) / kGemmGroupRows, ks);
-  float* out = ks > 1 ? (float*)ws : y;
-  hipLaunchKernelGGL(w4_gemm_kernel, grid, dim3(256), 0, st, (const uint16_t*)x, m, nib,
-                     scl, N, K, Q, qps, out);
+  uint16_t* xh = (uint16_t*)ws;
+  float* part = (float*)((uint8_t*)ws + gemm_xh_bytes(m, K));
+  const long long pieces = (long long)gemm_xh_bytes(m, K) / 16;
+  hipLaunchKernelGGL(w4_x_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)x, m, K, pieces, xh);
+  float* out = ks > 1 ? part : y;
+  hipLaunchKernelGGL(w4_gemm_kernel, grid, dim3(256), 0, st, xh, m, nib, scl, N, K, Q, qps, out);
   if (ks > 1) {
     const long long mn = (long long)m * N;
     hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
-                       (const float*)ws, ks, mn, y);
+                       part, ks, mn, y);
   }
   return hipGetLastError();
 }

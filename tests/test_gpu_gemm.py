@@ -1,6 +1,7 @@
 """GPU parity of the many-row int4 GEMM against the oracle's plain product
 (the same definition as the m-row GEMV, for a prefill's rows): relative L2
-per row within 1e-3, exact one-hot probes, k splits, ragged shapes,
+per row within 1e-3 (the GEMM multiplies fp16 operands: weights rounded once
+to fp16, which one-hot probes read back exactly), k splits, ragged shapes,
 determinism, agreement with the GEMV, and the 7B-like layer matrices at the
 254 rows of the agent-turn replay's turn 9, checked on sampled columns."""
 import numpy as np
@@ -55,12 +56,15 @@ def test_gemm_k_splits(splits):
     assert err.max() <= GEMM_TOL, err
 
 
-def test_gemm_one_hot_is_exact():
-    """x = e_c reads column c of the dequantised matrix exactly, for more
-    rows than the GEMV takes and across a k split."""
+def test_gemm_one_hot_reads_the_fp16_weights():
+    """x = e_c reads column c of the weights as the GEMM multiplies them:
+    (code - 8) * scale rounded once to fp16, for more rows than the GEMV
+    takes and across a k split."""
     n, k = 300, 1024
     w, s, packed = _weights(24, n, k)
-    dq = ow4.dequant(w, s, k)
+    codes = ow4.nibbles(w, k) - 8
+    scale = np.repeat(np.asarray(s, np.uint16).view(np.float16), 32, axis=1)
+    dq = (codes.astype(np.float16) * scale).astype(np.float64)  # one fp16 rounding
     cols = [0, 1, 7, 8, 31, 32, 127, 128, 129, 300, 511, 512, 700, 1000, 1023, 5, 64, 96, 255,
             256]
     x = np.zeros((len(cols), k), np.float32)
@@ -80,17 +84,11 @@ def test_gemm_zero_input_and_code8():
     w, s, packed = _weights(25, n, k)
     y = sve.w4_gemm(torch.zeros((40, k), dtype=torch.bfloat16, device="cuda"), packed, n, k)
     assert torch.count_nonzero(y).item() == 0
-    # code 8 everywhere: the exact product is 0; the kernel's group sum
-    # x.(128 + 8) - 136 sum(x) cancels up to the fp32 rounding of each term,
-    # at most 2^-22 of 136 sum|x| per group, times the group's scale
+    # code 8 everywhere: every weight is exactly 0
     w8 = synth.pack_nibbles(np.full((n, k), 8))
     p8 = sve.w4_pack(dev_u8(w8), dev_f16(s), n, k)
-    xb = synth.normal_bf16(synth.rng(26), (40, k))
-    y8 = sve.w4_gemm(dev_bf16(xb), p8, n, k).cpu().numpy().astype(np.float64)
-    xa = np.abs(ow4._bf16_to_f64(xb)).reshape(40, k // 32, 32).sum(axis=2)  # [m][groups]
-    sa = np.abs(ow4._fp16_to_f64(s))  # [n][groups]
-    bound = 136 * 2.0 ** -22 * xa @ sa.T
-    assert np.all(np.abs(y8) <= bound)
+    x = dev_bf16(synth.normal_bf16(synth.rng(26), (40, k)))
+    assert torch.count_nonzero(sve.w4_gemm(x, p8, n, k)).item() == 0
 
 
 def test_gemm_agrees_with_gemv_and_rows_are_independent():
@@ -124,7 +122,7 @@ def test_gemm_many_row_groups():
 def test_gemm_workspace_is_checked():
     m, n, k = 254, 4608, 3584
     need = sve.w4_gemm_workspace_bytes(m, n, k)
-    assert need > 0
+    assert need >= m * k * 2  # x in fp16, then the split partials
     w, s, packed = _weights(31, 64, 128)
     small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
     x = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
