@@ -358,6 +358,41 @@ def gemv_sweep(shapes, backlog, copies=8, m_values=range(1, 9), seed=3, reps=3):
     return res
 
 
+def prefill_gemm_sweep(shapes, backlog, m_values=(254, 134), copies=4, seed=5, reps=3):
+    """Many-row int4 GEMM (a prefill's projections): per m, each matrix's
+    calls (fp16 packing of x, the product, the k-split sum when used)
+    bracketed by HIP events, median over rotated weight copies and repeats."""
+    g = synth.rng(seed, 77)
+    mats = []
+    for (n, k) in shapes:
+        w, s = synth.w4_weights(g, n, k)
+        wd, sd = torch.from_numpy(w).cuda(), f16_dev(s)
+        mats.append((n, k, [sve.w4_pack(wd, sd, n, k) for _ in range(copies)]))
+        del wd, sd
+    kmax = max(k for _, k in shapes)
+    res = {}
+    for m in m_values:
+        x = bf16_dev(synth.normal_bf16(g, (m, kmax)))
+        per = {}
+        for (n, k, packs) in mats:
+            xk = x[:, :k].contiguous()
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            ws = torch.empty(sve.w4_gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device="cuda")
+            calls = [lambda c=c: sve.w4_gemm(xk, packs[c], n, k, y, ws) for c in range(copies)]
+            for f in calls:
+                f()
+            d = []
+            for _ in range(reps):
+                d += bracket(calls, backlog)
+            t = float(np.median(d))
+            fl = 2 * m * n * k
+            per[f"{n}x{k}"] = dict(us=t * 1e3, TFLOPs=fl / (t * 1e-3) / 1e12, flops=fl)
+        us = sum(v["us"] for v in per.values())
+        fl = sum(v["flops"] for v in per.values())
+        res[m] = dict(us=us, TFLOPs=fl / (us * 1e-6) / 1e12, flops=fl, per_matrix=per)
+    return res
+
+
 # ---------------------------------------------------------------------------
 # verify attention sweep (9B-like, 2048 cached)
 # ---------------------------------------------------------------------------
@@ -550,7 +585,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the GEMV / verify / MoE / slot sweeps")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the GEMV / GEMM / verify / MoE / slot sweeps")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the headline from eager launches only (for counter runs)")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
@@ -673,6 +709,24 @@ def main():
             "7b_layer_per_m": {m: {"us": r2(v["us"]), "GBps": round(v["GBps"], 1)}
                                for m, v in g7.items()},
         }
+        log("prefill gemm")
+        pg = prefill_gemm_sweep(synth.layer_gemv_shapes(3584, 18944, 28, 4, 128), backlog)
+        best = pg[254]["TFLOPs"]
+        out["prefill_gemm"] = {
+            "workload": "7B-like layer projections (QKV 4608x3584, O 3584x3584, gate|up "
+                        "37888x3584, down 3584x18944), int4 group-32 weights, m new rows "
+                        "(254: the replay's turn 9; 134: its turns 2-8); each call = fp16 "
+                        "packing of x + the product (+ the k-split sum), HIP events, 4 rotated "
+                        "weight copies; layer = sum of the four calls",
+            "roofline": {"bound": "mfma", "achieved": round(best, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(best / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "what": "m = 254, 2*m*N*K summed over the layer / summed call time; "
+                                 "peak = dense fp16 (= bf16) MFMA"},
+            "per_m": {m: {"us": r2(v["us"]), "TFLOPs": round(v["TFLOPs"], 1),
+                          "new_tok_per_s_layer": round(m / (v["us"] * 1e-6), 1),
+                          "per_matrix_us": {kk: r2(pv["us"]) for kk, pv in v["per_matrix"].items()}}
+                      for m, v in pg.items()}}
         log("verify sweep")
         vs = verify_sweep(backlog, layers=min(args.layers, ROT_LAYERS))
         a2, b2 = fit(list(vs), [vs[m]["attn_kernel_us"] for m in vs])
