@@ -48,12 +48,15 @@ def dequant(w: np.ndarray, scales: np.ndarray, k: int) -> np.ndarray:
 
 
 def gemv(x_bits: np.ndarray, w: np.ndarray, scales: np.ndarray, k: int) -> np.ndarray:
-    """y[r, n] = sum_k x[r, k] * w[n, k] in fp64, for bf16 x [m][K].
+    """y[r, n] = sum_k x[r, k] * w[n, k] in fp64, for bf16 x [m][K], any m.
 
     The m rows go through the same weight matrix (thinkspread, "The economics
     of speculative decoding", opening section: verify rows share one read of
-    the weights); the result is the ordinary product of each row with the
-    dequantised matrix. Computed in column chunks to bound memory."""
+    the weights; goinfer, "Turn nine in under half a second", section "The
+    problem": a prefill runs each new prompt token through every weight);
+    the result is the ordinary product of each row with the dequantised
+    matrix, the reference of both the m-row GEMV and the many-row GEMM.
+    Computed in column chunks to bound memory."""
     x = _bf16_to_f64(x_bits)
     assert x.ndim == 2 and x.shape[1] == k
     n = w.shape[0]
