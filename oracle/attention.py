@@ -86,6 +86,31 @@ def extend_attention_bruteforce(q_bits, k_bits, v_bits, prefix: int) -> np.ndarr
     return out
 
 
+def extend_attention_questions(q_bits, k_prefix_bits, v_prefix_bits, k_new_bits, v_new_bits,
+                               ms) -> np.ndarray:
+    """Several questions about one cached state (openjev-multimodal,
+    "Latency", section "What changed": with prefix priming the shared prefix
+    is evaluated once and each question resumes from that checkpoint,
+    reading only its own text).
+
+    The question rows are packed question after question (ms[j] rows each):
+    q [sum m][Hq][D], k_new / v_new [sum m][Hkv][D]; the prefix is
+    k_prefix / v_prefix [P][Hkv][D]. Question j is an ordinary extend of the
+    prefix by its own rows, so its row i sees prefix positions 0..P-1 and its
+    own rows 0..i, never another question's. Returns fp64 [sum m][Hq][D]."""
+    kp = np.asarray(k_prefix_bits)
+    vp = np.asarray(v_prefix_bits)
+    prefix = kp.shape[0]
+    out, r = [], 0
+    for m in ms:
+        rows = slice(r, r + int(m))
+        kk = np.concatenate([kp, np.asarray(k_new_bits)[rows]])
+        vv = np.concatenate([vp, np.asarray(v_new_bits)[rows]])
+        out.append(extend_attention(np.asarray(q_bits)[rows], kk, vv, prefix))
+        r += int(m)
+    return np.concatenate(out) if out else np.zeros((0,) + np.asarray(q_bits).shape[1:])
+
+
 def attention_flops(prefix: int, m: int, hq: int, d: int) -> int:
     """Algorithmic flops of one extend call: 2*D multiply-adds for q.k and
     2*D for p.v per visible (row, key) pair and query head."""
