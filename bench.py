@@ -393,6 +393,46 @@ def prefill_gemm_sweep(shapes, backlog, m_values=(254, 134), copies=4, seed=5, r
     return res
 
 
+def questions_sweep(backlog, layers=64, prefix=1250, ms=(30, 24, 36, 27), reps=3):
+    """Several questions about one state (4B-like heads): one questions call
+    per layer against the previous way, one extend per question with the
+    slot cut back to the state after each. HIP events per layer; the state
+    rotates over `layers` layers (5.1 MB of KV each)."""
+    hq, hkv, d = 32, 8, 128
+    total = int(sum(ms))
+    st = sve.KVSlots(1, layers, hq, hkv, d, prefix + 128, max(prefix, total))
+    st.kv_slot_select(np.arange(prefix + max(ms), dtype=np.int32))
+    c = synth.attention_case(71, hq, hkv, d, prefix, total)
+    qp, kp, vp = bf16_dev(c["q_prefix"]), bf16_dev(c["k_prefix"]), bf16_dev(c["v_prefix"])
+    for layer in range(layers):
+        st.extend_attn(0, layer, qp, kp, vp)
+    del qp, kp, vp
+    q, k, v = bf16_dev(c["q"]), bf16_dev(c["k"]), bf16_dev(c["v"])
+    out = torch.empty_like(q)
+    starts = np.concatenate([[0], np.cumsum(ms)[:-1]]).tolist()
+    parts = [(q[s0:s0 + m], k[s0:s0 + m], v[s0:s0 + m], out[s0:s0 + m]) for s0, m in zip(starts, ms)]
+
+    def together(layer):
+        st.extend_attn_questions(0, layer, list(ms), q, k, v, out)
+
+    def separate(layer):
+        for (qq, kk, vv, oo) in parts:
+            st.extend_attn(0, layer, qq, kk, vv, oo)
+            st.kv_truncate(0, prefix)
+
+    res = {}
+    for name, fn in (("one_call", together), ("per_question", separate)):
+        calls = [lambda L=L: fn(L) for L in range(layers)]
+        for f in calls[:4]:
+            f()
+        d = []
+        for _ in range(reps):
+            d += bracket(calls, backlog)
+        res[name] = float(np.median(d)) * 1e3
+    res["speedup"] = res["per_question"] / res["one_call"]
+    return res
+
+
 # ---------------------------------------------------------------------------
 # verify attention sweep (9B-like, 2048 cached)
 # ---------------------------------------------------------------------------
@@ -727,6 +767,15 @@ def main():
                           "new_tok_per_s_layer": round(m / (v["us"] * 1e-6), 1),
                           "per_matrix_us": {kk: r2(pv["us"]) for kk, pv in v["per_matrix"].items()}}
                       for m, v in pg.items()}}
+        log("questions")
+        qs = questions_sweep(backlog)
+        out["questions"] = {
+            "workload": "four questions (30, 24, 36, 27 rows) about one 1250-token state, 4B-like "
+                        "heads (32 q / 8 KV, D 128), 64 layers rotated; per-layer time from HIP "
+                        "events: one questions call (the state read once) against one extend per "
+                        "question with the slot cut back after each",
+            "one_call_us": r2(qs["one_call"]), "per_question_us": r2(qs["per_question"]),
+            "speedup": round(qs["speedup"], 3)}
         log("verify sweep")
         vs = verify_sweep(backlog, layers=min(args.layers, ROT_LAYERS))
         a2, b2 = fit(list(vs), [vs[m]["attn_kernel_us"] for m in vs])

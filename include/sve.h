@@ -140,6 +140,23 @@ int sve_extend_attn_batched(sve_ctx* ctx, int32_t n, const int32_t* slots_host,
                             const int32_t* m_host, int32_t layer, const void* q_packed,
                             const void* k_packed, const void* v_packed, void* out_packed);
 
+/* Several questions about one resident state ([openjev] "What changed",
+ * prefix priming: the shared prefix is evaluated once and each question
+ * resumes from it, reading only its own text). With P the cached length of
+ * (slot, layer), question j's rows i (0-based within the question) attend
+ * to positions 0..P-1 of the slot and to rows 0..i of question j only;
+ * scaling and GQA as sve_extend_attn. Nothing is appended: the cached
+ * length stays P and the slot's rows are only read, so the state remains
+ * the checkpoint for further questions.
+ *   n_questions: 1..16; m_host: host int32 [n_questions], each >= 1, sum
+ *   <= max_rows; q [sum m][Hq][D], new_k / new_v [sum m][Hkv][D] (the
+ *   questions' own rows), out [sum m][Hq][D]: device bf16, rows packed
+ *   question after question.
+ * Asynchronous. Errors: SVE_E_SLOT, SVE_E_ARG, SVE_E_CAPACITY, SVE_E_HIP. */
+int sve_extend_attn_questions(sve_ctx* ctx, int32_t slot, int32_t layer, int32_t n_questions,
+                              const int32_t* m_host, const void* q, const void* new_k,
+                              const void* new_v, void* out);
+
 /* Copy cached rows [start, start+len) of (slot, layer) to k_out, v_out:
  * device bf16 [len][Hkv][D] each (test export). */
 int sve_kv_read(sve_ctx* ctx, int32_t slot, int32_t layer, int32_t start, int32_t len,

@@ -140,6 +140,26 @@ class KVSlots:
             _ptr(out)), self.ctx)
         return out
 
+    def extend_attn_questions(self, slot: int, layer: int, ms, q: torch.Tensor,
+                              new_k: torch.Tensor, new_v: torch.Tensor,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+        """Several questions on the slot's resident prefix in one launch (rows
+        packed question after question); each sees the prefix and its own
+        rows; nothing is appended."""
+        ms = np.ascontiguousarray(np.asarray(ms, dtype=np.int32))
+        total = int(ms.sum())
+        _need(q, torch.bfloat16, (total, self.hq, self.d), "q")
+        _need(new_k, torch.bfloat16, (total, self.hkv, self.d), "new_k")
+        _need(new_v, torch.bfloat16, (total, self.hkv, self.d), "new_v")
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, torch.bfloat16, (total, self.hq, self.d), "out")
+        self._bind()
+        check(self._lib.sve_extend_attn_questions(
+            self.ctx, slot, layer, len(ms), ms.ctypes.data_as(C.c_void_p), _ptr(q), _ptr(new_k),
+            _ptr(new_v), _ptr(out)), self.ctx)
+        return out
+
     def timing_start(self, n_calls: int) -> None:
         """Record HIP events around the kernels of the next n_calls extend calls."""
         check(self._lib.sve_timing_start(self.ctx, int(n_calls)), self.ctx)

@@ -65,6 +65,7 @@ _SIGS = {
     "sve_extend_attn": (C.c_int, [_P, _I, _I, _P, _P, _P, _I, _P]),
     "sve_extend_attn_batched": (C.c_int, [_P, _I, _P, _P, _I, _P, _P, _P, _P]),
     "sve_kv_read": (C.c_int, [_P, _I, _I, _I, _I, _P, _P]),
+    "sve_extend_attn_questions": (C.c_int, [_P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "sve_w4_packed_bytes": (C.c_size_t, [_I, _I]),
     "sve_w4_pack": (C.c_int, [_P, _P, _I, _I, _P, _P]),
     "sve_w4_dequant": (C.c_int, [_P, _I, _I, _P, _P]),

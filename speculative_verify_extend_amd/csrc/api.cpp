@@ -183,9 +183,10 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
     sg.splits = std::max(S, 1);
     sg.split_keys = 64 * tps;
     sg.tail_split = 0;
-    sg.new_tile0 = fused ? sg.P / 64 : -1;
+    const bool fz = fused || sg.nq > 1;  // questions read their rows from the inputs
+    sg.new_tile0 = fz ? sg.P / 64 : -1;
     sg.append_begin = app;
-    sg.append_blocks = fused && sg.splits > 1 && sg.m > 0
+    sg.append_blocks = fused && sg.nq <= 1 && sg.splits > 1 && sg.m > 0
                            ? p.Hkv * ((sg.P + sg.m - 1) / 64 - sg.P / 64 + 1) * (p.D / 32)
                            : 0;
     app += sg.append_blocks;
@@ -381,6 +382,52 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
   if (e != hipSuccess) return hip_fail(c, e, "combine launch");
   if (ev) SVE_HIP(c, hipEventRecord(ev[3], c->stream));
   for (int i = 0; i < n; ++i) c->kv_len[slots[i]][layer] += ms[i];
+  return SVE_OK;
+}
+
+// Several questions on one slot's resident prefix, one MFMA launch (plus the
+// combine): nothing is appended and kv_len stays.
+int run_questions(sve_ctx* c, int slot, int layer, int nq, const int32_t* ms,
+                  const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out) {
+  const sve_config& cf = c->cfg;
+  if (slot < 0 || slot >= c->granted) return fail(c, SVE_E_SLOT, "slot out of range");
+  if (layer < 0 || layer >= cf.n_layers) return fail(c, SVE_E_SLOT, "layer out of range");
+  if (nq < 1 || nq > kMaxQuestions) return fail(c, SVE_E_ARG, "questions must be 1..16");
+  if (!ms) return fail(c, SVE_E_ARG, "null question sizes");
+  long long total = 0;
+  for (int j = 0; j < nq; ++j) {
+    if (ms[j] < 1) return fail(c, SVE_E_ARG, "every question needs at least one row");
+    total += ms[j];
+  }
+  if (total > cf.max_rows) return fail(c, SVE_E_CAPACITY, "more rows than max_rows");
+  if (!q || !k || !v || !out) return fail(c, SVE_E_ARG, "null tensor pointer");
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.Hq = cf.n_q_heads;
+  p.Hkv = cf.n_kv_heads;
+  p.g = p.Hq / p.Hkv;
+  p.D = cf.head_dim;
+  p.cap = c->lay.cap;
+  p.c = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+  p.nseg = 1;
+  AttnSeg& sg = p.seg[0];
+  sg.K = c->kbase(slot, layer);
+  sg.Vt = c->vtbase(slot, layer);
+  sg.q = q;
+  sg.nk = k;
+  sg.nv = v;
+  sg.out = out;
+  sg.P = c->kv_len[slot][layer];
+  sg.m = (int)total;
+  sg.nq = nq;
+  for (int j = 0, r = 0; j < nq; r += ms[j], ++j) sg.qstart[j] = r;
+  sg.row_blocks = (sg.m * p.g + attn_rows_per_block(kPathMfma) - 1) / attn_rows_per_block(kPathMfma);
+  p.total_rows_hint = sg.m;
+  plan_mfma(c, p);
+  hipError_t e = launch_attn(p, kPathMfma, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "questions attention launch");
+  e = launch_attn_combine(p, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "questions combine launch");
   return SVE_OK;
 }
 
@@ -619,6 +666,14 @@ int sve_extend_attn_batched(sve_ctx* c, int32_t n, const int32_t* slots, const i
   if (!slots || !ms) return fail(c, SVE_E_ARG, "null pointer");
   return run_extend(c, n, slots, ms, layer, (const uint16_t*)q, (const uint16_t*)k,
                     (const uint16_t*)v, (uint16_t*)out);
+}
+
+int sve_extend_attn_questions(sve_ctx* ctx, int32_t slot, int32_t layer, int32_t n_questions,
+                              const int32_t* m_host, const void* q, const void* new_k,
+                              const void* new_v, void* out) {
+  if (!ctx) return fail(nullptr, SVE_E_ARG, "null context");
+  return run_questions(ctx, slot, layer, n_questions, m_host, (const uint16_t*)q,
+                       (const uint16_t*)new_k, (const uint16_t*)new_v, (uint16_t*)out);
 }
 
 int sve_kv_read(sve_ctx* c, int32_t slot, int32_t layer, int32_t start, int32_t len, void* k_out,

@@ -276,8 +276,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   f32x4 S[RT][2][2];
   bf16x8 pb[RT][2];
   // online softmax of tile t: mask, running max, rescale, bf16 probabilities
-  auto softmax = [&](int kt, auto edge_tag) {
+  // lower end of the new keys a row sees (epilogue only): P + the start of
+  // its question; P for an ordinary extend
+  int blo[RT];
+  auto softmax = [&](int kt, auto edge_tag, auto band_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr bool BAND = decltype(band_tag)::value;
     bool grow = false;
     float mcand[RT];
 #pragma unroll
@@ -292,7 +296,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
             float v = S[rt][c][sub][i];
             if constexpr (EDGE) {
               const int key = kt + 32 * c + 8 * kb + 4 * sub + i;
-              v = (key <= lim[rt]) ? v : -INFINITY;
+              bool vis = key <= lim[rt];
+              if constexpr (BAND) vis = vis && (key < P || key >= blo[rt]);
+              v = vis ? v : -INFINITY;
               S[rt][c][sub][i] = v;
             }
             mx = fmaxf(mx, v);
@@ -438,9 +444,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       // Keys past a row's causal limit only occur in tiles that reach beyond
       // the smallest limit of the workgroup's rows; only those mask.
       if (tile_kt(j) + 63 > wg_min_lim)
-        softmax(tile_kt(j), std::true_type{});
+        softmax(tile_kt(j), std::true_type{}, std::false_type{});
       else
-        softmax(tile_kt(j), std::false_type{});
+        softmax(tile_kt(j), std::false_type{}, std::false_type{});
       if (k2)
         wait_vmem<2 * NV>();
       else
@@ -450,9 +456,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       stage_end();
     }
     if (tile_kt(n - 1) + 63 > wg_min_lim)
-      softmax(tile_kt(n - 1), std::true_type{});
+      softmax(tile_kt(n - 1), std::true_type{}, std::false_type{});
     else
-      softmax(tile_kt(n - 1), std::false_type{});
+      softmax(tile_kt(n - 1), std::false_type{}, std::false_type{});
     wait_vmem<0>();
     stage_end();
     mstage(n - 1, 0, std::true_type{}, std::false_type{});
@@ -489,6 +495,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     // with the prologue's, which would keep them live through the key loop
     const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 63;
     const int gt = gw * 64 + ln;  // thread within the key group
+    // each row's question (several questions: rows of question j see the
+    // prefix and the rows of question j only), from the fresh lane index
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int i = min(wg_row0 + gw * 16 * RT + 16 * rt + (ln & 15), R - 1) / g;
+      int s0 = 0;
+#pragma unroll
+      for (int j = 1; j < kMaxQuestions; ++j)
+        if (j < sg.nq && i >= sg.qstart[j]) s0 = sg.qstart[j];
+      blo[rt] = P + s0;
+    }
     const int wt = wave * 64 + ln;  // thread within the workgroup
     constexpr int ITEMS = CPR / 4;  // 16-byte pieces per thread per tile part
     uint16_t* Vr = lds[grp][0][1];  // the call's V rows as loaded
@@ -556,7 +573,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       requests(r0 + 2);  // into the other K buffer and the now free row buffer
       if (has) {
         mstage(0, (r0 >> 1) & 1, std::false_type{}, std::true_type{});
-        softmax(kt, std::true_type{});
+        softmax(kt, std::true_type{}, std::true_type{});
         mstage(1, 0, std::true_type{}, std::false_type{});
       }
       __syncthreads();
@@ -569,7 +586,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     // distinct banks) and leave as 16-byte pieces of 8 keys of one column,
     // key by key in the pieces holding P or P+m.
     const int A = min(sg.row_blocks, kAppendBlocks);
-    if (sg.splits == 1 && rb < A) {
+    if (sg.splits == 1 && sg.nq <= 1 && rb < A) {
       constexpr int VST = D + 2;
       uint16_t* Va = &lds[0][0][0][0];  // [64][VST]
       const uint16_t* nkh = sg.nk + (size_t)kvh * D;
@@ -1211,7 +1228,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams prm) {
 
 // ---------------------------------------------------------------------------
 // Split combine: out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s over
-// the splits that contain at least one key the row can see, in split order,
+// the splits that start at or before the row's last key (one that holds no
+// key the row sees has l_s = 0 and weighs exactly 0), in split order,
 // with o_s = O_s / l_s the split's normalised output (stored in fp16 times
 // its scale s_s).
 // grid over rows (i, h) of all pieces; 4 columns per thread.
@@ -1326,10 +1344,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= r;
     M = Mb;
+    // a split with no key this row sees (several questions: a split inside
+    // another question's rows) has max -inf and sum 0; with every split so
+    // far like that, M is -inf too and the weight must still come out 0
+    const float Mu = (M == -INFINITY) ? 0.f : M;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const bool ok = (b0 + u) * PARTS + part < nvalid;
-      const float sc = fast_exp2(ml[u][0] - M);
+      const float sc = fast_exp2(ml[u][0] - Mu);
       const float wl = ok ? sc * ml[u][1] : 0.f;
       const float wo = ok ? wl * ml[u][2] : 0.f;
       l += wl;

@@ -25,6 +25,7 @@ hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int
 
 // ---- attention ------------------------------------------------------------------
 constexpr int kMaxSeg = 4;
+constexpr int kMaxQuestions = 16;
 
 // One (slot, layer) piece of an extend call. The KV store of a slot and layer
 // is K [Hkv][cap][D] followed by Vt [Hkv][D][cap] (bf16).
@@ -57,6 +58,12 @@ struct AttnSeg {
   // attention kernel. -1: every key is in the store, appended beforehand.
   int new_tile0;
   int append_blocks, append_begin;
+  // several questions on one prefix (MFMA path): the m rows are nq
+  // questions starting at rows qstart[0] = 0 < qstart[1] < ...; a row sees
+  // the prefix [0, P) and the rows of its own question up to itself, and
+  // nothing is appended. nq <= 1: an ordinary extend.
+  int nq;
+  int qstart[kMaxQuestions];
   int block_begin;     // first linear workgroup of this piece
   int row_begin;       // first output row of this piece in a combined launch
 };
