@@ -314,6 +314,22 @@ int sve_timing_start(sve_ctx* ctx, int32_t n_calls);
 int sve_timing_read(sve_ctx* ctx, float* append_ms, float* attn_ms, float* combine_ms,
                     int32_t* calls);
 
+/* ---- prompt-lookup drafting ([goinfer] "What we got wrong": with n-gram
+ * speculation the runtime guesses the next tokens from text already in the
+ * prompt and checks them in one verify step) ----------------------------------
+ * Host-only integer search. For suffix lengths g = min(max_ngram, n-1) down
+ * to min_ngram, finds the latest earlier start p (p = n-g-1 down to 0;
+ * overlapping the suffix is allowed) with tokens[p..p+g) equal to the last
+ * g tokens, and writes the up to k tokens that followed it
+ * (tokens[p+g .. p+g+k), fewer at the end of the history) to draft_host;
+ * *n_draft = their count, 0 when no suffix of any length occurred before.
+ *   tokens_host: host int32 [n], n >= 0; draft_host: host int32 [k];
+ *   0 <= k <= SVE_NGRAM_MAX_DRAFT, 1 <= min_ngram <= max_ngram <= 64.
+ * Errors: SVE_E_ARG. */
+#define SVE_NGRAM_MAX_DRAFT 64
+int sve_ngram_draft(const int32_t* tokens_host, int32_t n, int32_t k, int32_t max_ngram,
+                    int32_t min_ngram, int32_t* draft_host, int32_t* n_draft);
+
 /* Message for a status code. */
 const char* sve_strerror(int code);
 

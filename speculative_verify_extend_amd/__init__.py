@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import SveError, check
 
-__all__ = ["KVSlots", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m", "w4_gemm",
+__all__ = ["KVSlots", "ngram_draft", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m", "w4_gemm",
            "w4_gemm_workspace_bytes",
            "w4_gemv_m_routed", "verify_workspace_bytes", "verify_accept", "SpecGate",
            "spec_break_even", "probe_read", "probe_copy", "SveError", "load_library"]
@@ -260,6 +260,19 @@ def w4_gemv_m_routed(x: torch.Tensor, expert_ids: torch.Tensor, packed_all: torc
     check(lib.sve_w4_gemv_m_routed(_ptr(x), int(bool(x_per_slot)), m, _ptr(expert_ids), topk,
                                    _ptr(packed_all), n_experts, n, k, _ptr(y), _stream()))
     return y
+
+
+def ngram_draft(tokens, k: int, max_ngram: int = 3, min_ngram: int = 1) -> np.ndarray:
+    """Prompt-lookup draft: the up to k tokens that followed the latest
+    earlier occurrence of the history's longest repeated suffix (host)."""
+    lib = _lib.load()
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    out = np.zeros(max(int(k), 1), dtype=np.int32)
+    cnt = C.c_int32(0)
+    check(lib.sve_ngram_draft(t.ctypes.data_as(C.c_void_p) if t.size else None, int(t.size),
+                              int(k), int(max_ngram), int(min_ngram),
+                              out.ctypes.data_as(C.c_void_p), C.byref(cnt)))
+    return out[:cnt.value].copy()
 
 
 def verify_workspace_bytes(m: int, vocab: int) -> int:

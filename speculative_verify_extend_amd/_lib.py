@@ -79,6 +79,7 @@ _SIGS = {
     "sve_timing_read": (C.c_int, [_P, C.POINTER(C.c_float), C.POINTER(C.c_float),
                                   C.POINTER(C.c_float), C.POINTER(_I)]),
     "sve_verify_workspace_bytes": (C.c_size_t, [_I, _I]),
+    "sve_ngram_draft": (C.c_int, [_P, _I, _I, _I, _I, _P, C.POINTER(_I)]),
     "sve_verify_accept": (C.c_int, [_P, _I, _I, _P, _P, _P, C.c_size_t, _P]),
     "sve_spec_gate_init": (C.c_int, [_P, _I, C.c_double, _I]),
     "sve_spec_gate_step": (C.c_int, [_P, _I, C.POINTER(_I)]),

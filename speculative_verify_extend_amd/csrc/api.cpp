@@ -752,6 +752,31 @@ int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int
   return SVE_OK;
 }
 
+int sve_ngram_draft(const int32_t* tokens, int32_t n, int32_t k, int32_t max_ngram,
+                    int32_t min_ngram, int32_t* draft, int32_t* n_draft) {
+  if (n < 0 || k < 0 || k > SVE_NGRAM_MAX_DRAFT) return fail(nullptr, SVE_E_ARG, "bad n or k");
+  if (min_ngram < 1 || max_ngram < min_ngram || max_ngram > 64)
+    return fail(nullptr, SVE_E_ARG, "need 1 <= min_ngram <= max_ngram <= 64");
+  if (!n_draft || (n > 0 && !tokens) || (k > 0 && !draft))
+    return fail(nullptr, SVE_E_ARG, "null pointer");
+  *n_draft = 0;
+  if (k == 0) return SVE_OK;
+  // longest suffix first; for each length the latest earlier start
+  for (int g = std::min(max_ngram, n - 1); g >= min_ngram; --g) {
+    const int32_t* suffix = tokens + (n - g);
+    for (int p = n - g - 1; p >= 0; --p) {
+      if (tokens[p + g - 1] != suffix[g - 1] || tokens[p] != suffix[0]) continue;
+      if (std::equal(tokens + p, tokens + p + g, suffix)) {
+        const int cnt = std::min(k, n - (p + g));
+        std::copy(tokens + p + g, tokens + p + g + cnt, draft);
+        *n_draft = cnt;
+        return SVE_OK;
+      }
+    }
+  }
+  return SVE_OK;
+}
+
 size_t sve_verify_workspace_bytes(int32_t m, int32_t V) {
   if (m < 1 || m > SVE_VERIFY_MAX_ROWS || V < 1) return 0;
   return verify_workspace_bytes(m, V);
