@@ -136,15 +136,14 @@ int hip_fail(const sve_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(ctx, e_, #expr); \
   } while (0)
 
-// MFMA path. Split s of a piece holds the 64-key tiles [s, s+1) * tps, and
-// row block rb (128 packed rows) gets a workgroup for split s only when its
-// last row sees a key there: the first such row block is g * X / 128 with
-// X = 64 * s * tps - P (row i sees keys up to P + i). Every workgroup then
-// holds at most tps tiles and none is empty. tps is the smallest value that
-// keeps the grid within one round of workgroups on the 256 compute units
-// (and at most 16 splits, what the workspace holds per row).
+// MFMA path. A row block (128 packed rows) gets a workgroup for a split only
+// when its last row sees a key there: for a split starting at key P + X the
+// first such row block is g * X / 128 (row i sees keys up to P + i), so no
+// workgroup is empty.
 int mfma_first_block(int X, int g) { return X > 0 ? (int)(((long long)g * X) / 128) : 0; }
 
+// Uniform layout (every key in the store): split s holds tiles
+// [s, s+1) * tps. Returns workgroups per KV head; *splits = the count.
 int mfma_head_blocks(const AttnSeg& sg, int g, int tps, int* splits) {
   const int S = sg.m > 0 ? ((sg.P + sg.m - 1) / 64 + 1 + tps - 1) / tps : 0;
   int hb = 0;
@@ -153,38 +152,126 @@ int mfma_head_blocks(const AttnSeg& sg, int g, int tps, int* splits) {
   return hb;
 }
 
+// Cached/new layout (new keys read from the call's inputs): S1 pieces cut
+// the cached tiles [0, nt0) evenly, then pieces of tpn new tiles. A cached
+// tile runs in the staged loop, a new tile in the slower epilogue, so no
+// piece mixes the two. Returns workgroups per KV head; *splits = S1 + new
+// pieces.
+int mfma_head_blocks_cn(const AttnSeg& sg, int g, int S1, int tpn, int* splits) {
+  const int nt0 = sg.P / 64;
+  const int new_max = sg.m > 0 ? (sg.P + sg.m - 1) / 64 + 1 - nt0 : 0;
+  const int S2 = (new_max + tpn - 1) / tpn;
+  int hb = S1 * sg.row_blocks;
+  for (int n = 0; n < S2; ++n) hb += sg.row_blocks - mfma_first_block(64 * (nt0 + n * tpn) - sg.P, g);
+  if (splits) *splits = S1 + S2;
+  return hb;
+}
+
+// Estimated time (us) of one workgroup's piece, fitted to per-workgroup
+// timestamps of the turn-9 shapes: 5.8 fixed (arguments, query loads, the
+// merge and partial stores), 1.3 per cached tile in the staged loop, 4.0 +
+// 1.6 per new tile in the epilogue (its first round waits for the call's
+// rows).
+double mfma_piece_us(int cached, int fresh) {
+  return 5.8 + 1.3 * cached + (fresh > 0 ? 4.0 + 1.6 * fresh : 0.0);
+}
+
 void plan_mfma(sve_ctx* c, AttnParams& p) {
-  constexpr int kTarget = 256;
+  constexpr int kTarget = 256;  // one workgroup per CU (128 KB of LDS each)
   const int g = p.g;
-  int tmax = 1;
-  for (int s = 0; s < p.nseg; ++s)
-    if (p.seg[s].m > 0) tmax = std::max(tmax, (p.seg[s].P + p.seg[s].m - 1) / 64 + 1);
-  int tps = std::max(1, (tmax + kMaxSplits - 1) / kMaxSplits);
-  const int forced = env_int("SVE_KV_SPLIT", 0);
-  if (forced > 0) {
-    tps = std::max(tps, (tmax + forced - 1) / forced);
-  } else {
-    for (;; ++tps) {
-      long long blocks = 0;
-      for (int s = 0; s < p.nseg; ++s) blocks += (long long)p.Hkv * mfma_head_blocks(p.seg[s], g, tps, nullptr);
-      if (blocks <= kTarget || tps >= tmax) break;
-    }
-  }
   // the attention kernel reads the new rows from the call's inputs; they
   // are appended by the combine kernel (split pieces) or by the attention
   // kernel itself (unsplit pieces)
   const bool fused = env_int("SVE_FUSED_APPEND", 1) != 0;
+  const int forced = env_int("SVE_KV_SPLIT", 0);
+  // SVE_ATTN_LAYOUT: 0 chooses, 1 forces the uniform layout, 2 the
+  // cached/new one (where the new rows come from the inputs)
+  const int layout = env_int("SVE_ATTN_LAYOUT", 0);
+  bool cn_ok = forced <= 0;
+  for (int s = 0; s < p.nseg; ++s) cn_ok &= (fused || p.seg[s].nq > 1);
+  // uniform layout: the fewest tiles per split that keep the grid within one
+  // round of workgroups
+  int tps = 1, S1 = 0, tpn = 1;
+  long long uniform_blocks = 0;
+  {
+    int tmax = 1;
+    for (int s = 0; s < p.nseg; ++s)
+      if (p.seg[s].m > 0) tmax = std::max(tmax, (p.seg[s].P + p.seg[s].m - 1) / 64 + 1);
+    tps = std::max(1, (tmax + kMaxSplits - 1) / kMaxSplits);
+    if (forced > 0) tps = std::max(tps, (tmax + forced - 1) / forced);
+    for (;; ++tps) {
+      uniform_blocks = 0;
+      for (int s = 0; s < p.nseg; ++s)
+        uniform_blocks += (long long)p.Hkv * mfma_head_blocks(p.seg[s], g, tps, nullptr);
+      if (forced > 0 || uniform_blocks <= kTarget || tps >= tmax) break;
+    }
+  }
+  // cached/new layout where the uniform one needs more than one round (a
+  // long suffix over a short prefix): measured per-workgroup times show a
+  // piece mixing cached and new tiles costs less than the piece model below
+  // says, so the uniform layout stays where it fits
+  const bool cn = cn_ok && layout != 1 && (layout == 2 || uniform_blocks > kTarget);
+  if (cn) {
+    // the (S1, tpn) with the least estimated time: the slowest piece times
+    // the rounds of workgroups the grid needs
+    int new_max = 1, nt0_max = 0;
+    for (int s = 0; s < p.nseg; ++s) {
+      const AttnSeg& sg = p.seg[s];
+      if (sg.m <= 0) continue;
+      nt0_max = std::max(nt0_max, sg.P / 64);
+      new_max = std::max(new_max, (sg.P + sg.m - 1) / 64 + 1 - sg.P / 64);
+    }
+    double best = 1e30;
+    long long best_wg = 0;
+    for (int a = (nt0_max > 0 ? 1 : 0); a <= std::min(nt0_max, kMaxSplits - 1); ++a)
+      for (int b = 1; b <= new_max; ++b) {
+        long long wg = 0;
+        double worst = 0;
+        bool ok = true;
+        for (int s = 0; s < p.nseg && ok; ++s) {
+          const AttnSeg& sg = p.seg[s];
+          if (sg.m <= 0) continue;
+          const int nt0 = sg.P / 64, s1 = nt0 > 0 ? std::min(a, nt0) : 0;
+          int S = 0;
+          wg += (long long)p.Hkv * mfma_head_blocks_cn(sg, g, s1, b, &S);
+          ok = S <= kMaxSplits;
+          const int nm = (sg.P + sg.m - 1) / 64 + 1 - nt0;
+          if (s1 > 0) worst = std::max(worst, mfma_piece_us((nt0 + s1 - 1) / s1, 0));
+          worst = std::max(worst, mfma_piece_us(0, std::min(b, nm)));
+        }
+        if (!ok) continue;
+        const double est = worst * (double)((wg + kTarget - 1) / kTarget);
+        if (est < best - 1e-9 || (est < best + 1e-9 && wg < best_wg)) {
+          best = est;
+          best_wg = wg;
+          S1 = a;
+          tpn = b;
+        }
+      }
+    S1 = env_int("SVE_STAGE_PIECES", S1);
+    tpn = std::max(1, env_int("SVE_NEW_TILES_PER_PIECE", tpn));
+  }
   long long ws_rows = 0;
   int blocks = 0, rows = 0, app = 0;
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
     int S = 0;
-    sg.head_blocks = mfma_head_blocks(sg, g, tps, &S);
-    sg.splits = std::max(S, 1);
-    sg.split_keys = 64 * tps;
-    sg.tail_split = 0;
     const bool fz = fused || sg.nq > 1;  // questions read their rows from the inputs
     sg.new_tile0 = fz ? sg.P / 64 : -1;
+    if (cn) {
+      const int nt0 = sg.P / 64;
+      sg.stage_pieces = nt0 > 0 ? std::max(1, std::min(S1, nt0)) : 0;
+      sg.new_tpp = tpn;
+      sg.head_blocks = mfma_head_blocks_cn(sg, g, sg.stage_pieces, tpn, &S);
+      sg.split_keys = 64;  // (unused by this layout)
+    } else {
+      sg.stage_pieces = -1;
+      sg.new_tpp = 1;
+      sg.head_blocks = mfma_head_blocks(sg, g, tps, &S);
+      sg.split_keys = 64 * tps;
+    }
+    sg.splits = std::max(S, 1);
+    sg.tail_split = 0;
     sg.append_begin = app;
     sg.append_blocks = fused && sg.nq <= 1 && sg.splits > 1 && sg.m > 0
                            ? p.Hkv * ((sg.P + sg.m - 1) / 64 - sg.P / 64 + 1) * (p.D / 32)
@@ -202,8 +289,8 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
   p.total_rows = rows;
   p.append_total = app;
   if (log_on()) {
-    fprintf(stderr, "[sve] extend: path=mfma pieces=%d blocks=%d tiles/split=%d append=%d", p.nseg,
-            blocks, tps, app);
+    fprintf(stderr, "[sve] extend: path=mfma pieces=%d blocks=%d layout=%s S1=%d tpn=%d tps=%d append=%d",
+            p.nseg, blocks, cn ? "cached/new" : "uniform", S1, tpn, tps, app);
     for (int s = 0; s < p.nseg; ++s)
       fprintf(stderr, " (P=%d m=%d splits=%d)", p.seg[s].P, p.seg[s].m, p.seg[s].splits);
     fprintf(stderr, "\n");
@@ -283,6 +370,8 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     sg.tail_split = dec ? 1 : 0;
     sg.new_tile0 = -1;
     sg.head_blocks = sg.row_blocks * S;
+    sg.stage_pieces = -1;  // uniform splits (the combine's range rule)
+    sg.new_tpp = 1;
     sg.append_blocks = sg.append_begin = 0;
     sg.block_begin = blocks;
     sg.row_begin = rows;

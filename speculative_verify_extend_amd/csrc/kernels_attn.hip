@@ -137,12 +137,15 @@ __device__ __forceinline__ int kswz(int key, int c) {
 }
 __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
 
-// ONE: the call has a single piece (its fields load without first finding
-// the piece, one scalar round trip less)
 // row-block workgroups of the last split that append the call's rows
 constexpr int kAppendBlocks = 4;
 
-template <int D, int RT, bool ONE>
+// ONE: the call has a single piece (its fields load without first finding
+// the piece, one scalar round trip less). QB: several questions about one
+// state, so a new row also masks the new rows of the other questions (kept
+// out of the ordinary variant: the band costs a calls' epilogue about a
+// microsecond)
+template <int D, int RT, bool ONE, bool QB>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   constexpr int DC = D / 32;
   constexpr int DT = D / 16;
@@ -156,21 +159,35 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   const AttnSeg& sg = prm.seg[ONE ? 0 : ref.s];
   const int g = prm.g, Hq = prm.Hq, cap = prm.cap;
   const int P = sg.P, m = sg.m, R = m * g;
-  // split-major within a KV head: split s has a workgroup for each row block
-  // from the first one whose last row sees a key of the split's tiles
-  const int tps = sg.split_keys / 64;
+  // split-major within a KV head: a split has a workgroup for each row block
+  // from the first one whose last row sees a key of the split's tiles (the
+  // first such block: g * X / (64 RT) for the split's first key P + X)
   const int kvh = ref.local / sg.head_blocks;
-  int split = 0, rb = 0;
+  const int nt0s = sg.new_tile0, S1 = sg.stage_pieces, tpn = sg.new_tpp;
+  int split = 0, rb = 0, t_lo = 0, t_hi = 0;
   {
     int j = ref.local - kvh * sg.head_blocks;
-    for (; split < sg.splits; ++split) {
-      const int X = 64 * split * tps - P;
-      const int rb0 = X > 0 ? (g * X) / (64 * RT) : 0;
-      if (j < sg.row_blocks - rb0) {
-        rb = rb0 + j;
-        break;
+    if (S1 >= 0 && j < S1 * sg.row_blocks) {  // a piece of the cached tiles
+      split = j / sg.row_blocks;
+      rb = j - split * sg.row_blocks;
+      t_lo = split * nt0s / S1;
+      t_hi = (split + 1) * nt0s / S1;
+    } else {
+      const int tps = S1 >= 0 ? tpn : sg.split_keys / 64;
+      const int tbase = S1 >= 0 ? nt0s : 0;
+      if (S1 >= 0) j -= S1 * sg.row_blocks;
+      for (int n = 0; n < sg.splits; ++n) {
+        const int X = 64 * (tbase + n * tps) - P;
+        const int rb0 = X > 0 ? (g * X) / (64 * RT) : 0;
+        if (j < sg.row_blocks - rb0) {
+          split = (S1 >= 0 ? S1 : 0) + n;
+          rb = rb0 + j;
+          t_lo = tbase + n * tps;
+          t_hi = t_lo + tps;
+          break;
+        }
+        j -= sg.row_blocks - rb0;
       }
-      j -= sg.row_blocks - rb0;
     }
   }
 
@@ -181,15 +198,15 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
 
   const int wg_row0 = rb * 64 * RT;
   const int wg_last = min(R - 1, wg_row0 + 64 * RT - 1);
-  // 64-key tiles [64T, 64T+64); a split is a run of tps of them. With
+  // 64-key tiles [64T, 64T+64); a split is a run of them [t_lo, t_hi). With
   // new_tile0 >= 0 the tiles from new_tile0 = P / 64 on go through the
   // epilogue, which reads keys at or past P from the call's rows; the others
   // come from the store through the staged loop.
   const int nt0 = sg.new_tile0;
   const bool fused = nt0 >= 0;
   const int t_rows = (P + wg_last / g) / 64 + 1;  // tiles any row of the block sees
-  const int t_begin = split * tps;
-  const int t_end = min(t_begin + tps, t_rows);
+  const int t_begin = t_lo;
+  const int t_end = min(t_hi, t_rows);
   if (t_begin >= t_end) return;  // (not launched: no row of the block sees the split)
   const int wg_min_lim = P + wg_row0 / g;
   const int t_cend = fused ? max(t_begin, min(t_end, nt0)) : t_end;
@@ -296,8 +313,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
             float v = S[rt][c][sub][i];
             if constexpr (EDGE) {
               const int key = kt + 32 * c + 8 * kb + 4 * sub + i;
+              // (bitwise, not short-circuit: no branch per element)
               bool vis = key <= lim[rt];
-              if constexpr (BAND) vis = vis && (key < P || key >= blo[rt]);
+              if constexpr (BAND) vis = vis & ((key < P) | (key >= blo[rt]));
               v = vis ? v : -INFINITY;
               S[rt][c][sub][i] = v;
             }
@@ -496,15 +514,18 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 63;
     const int gt = gw * 64 + ln;  // thread within the key group
     // each row's question (several questions: rows of question j see the
-    // prefix and the rows of question j only), from the fresh lane index
+    // prefix and the rows of question j only), from the fresh lane index;
+    // only the questions variant has the band
+    if constexpr (QB) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int i = min(wg_row0 + gw * 16 * RT + 16 * rt + (ln & 15), R - 1) / g;
-      int s0 = 0;
+      for (int rt = 0; rt < RT; ++rt) {
+        const int i = min(wg_row0 + gw * 16 * RT + 16 * rt + (ln & 15), R - 1) / g;
+        int s0 = 0;
 #pragma unroll
-      for (int j = 1; j < kMaxQuestions; ++j)
-        if (j < sg.nq && i >= sg.qstart[j]) s0 = sg.qstart[j];
-      blo[rt] = P + s0;
+        for (int j = 1; j < kMaxQuestions; ++j)
+          if (j < sg.nq && i >= sg.qstart[j]) s0 = sg.qstart[j];
+        blo[rt] = P + s0;
+      }
     }
     const int wt = wave * 64 + ln;  // thread within the workgroup
     constexpr int ITEMS = CPR / 4;  // 16-byte pieces per thread per tile part
@@ -573,7 +594,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       requests(r0 + 2);  // into the other K buffer and the now free row buffer
       if (has) {
         mstage(0, (r0 >> 1) & 1, std::false_type{}, std::true_type{});
-        softmax(kt, std::true_type{}, std::true_type{});
+        softmax(kt, std::true_type{}, std::bool_constant<QB>{});
         mstage(1, 0, std::true_type{}, std::false_type{});
       }
       __syncthreads();
@@ -1314,8 +1335,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int i = grow - sg.row_begin;
   // uniform splits: those starting at or before the row's last key; the
   // decode layout (cached splits + one new-key split): all of them
+  // (cached pieces and new-tile pieces: every cached piece, then the new
+  // pieces starting at or before the row's last tile)
   const int nvalid =
-      sg.tail_split ? sg.splits : min(sg.splits, (sg.P + i) / sg.split_keys + 1);
+      sg.tail_split ? sg.splits
+      : sg.stage_pieces >= 0
+          ? min(sg.splits, sg.stage_pieces + ((sg.P + i) / 64 - sg.new_tile0) / sg.new_tpp + 1)
+          : min(sg.splits, (sg.P + i) / sg.split_keys + 1);
   const float* mlp = sg.ws_ml + ((size_t)i * p.Hq + h) * 4;
   const uint16_t* op = sg.ws_o + ((size_t)i * p.Hq + h) * D + c4;
   const size_t ml_stride = (size_t)sg.m * p.Hq * 4, o_stride = (size_t)sg.m * p.Hq * D;
@@ -1434,7 +1460,14 @@ static void launch_decode(const AttnParams& p, int rt, int ns, hipStream_t st) {
 
 template <int D, bool ONE>
 static void launch_mfma(const AttnParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, 2, ONE>), dim3(p.total_blocks), dim3(512), 0, st, p);
+  // several questions about one state: the variant with the question band
+  // (always a single piece list)
+  if (ONE && p.seg[0].nq > 1)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, true, true>), dim3(p.total_blocks), dim3(512), 0,
+                       st, p);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, ONE, false>), dim3(p.total_blocks), dim3(512), 0,
+                       st, p);
 }
 
 template <int D, bool ONE>
