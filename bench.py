@@ -291,6 +291,49 @@ class Replay:
         self.graph.replay()
 
 
+def replay_turns(rp, passes=2, n_inputs=4):
+    """Every turn of the agent replay on the replay's store and rotated
+    layers: turn t cuts the slot back to L_(t-1) resident rows (metadata
+    only) and extends its m = L_t - L_(t-1) new rows in every layer. The
+    slot's committed prompt is turn 9's, which starts with every earlier
+    prompt, so no select is needed between turns. Per call: the kernel
+    durations the library records with HIP events (eager calls). The new
+    rows rotate over a few input buffers; the KV read per layer is the
+    store's, distinct per layer."""
+    wl = synth.WORKLOADS["replay7b"]
+    lengths = list(wl["prompt_lengths"])[:9]  # turn 10's length is an extrapolation
+    starts = [0] + lengths[:-1]
+    mmax = max(b - a for a, b in zip(starts, lengths))
+    g = synth.rng(wl["seed"], 91)
+    ins = [tuple(bf16_dev(a) for a in synth.attention_rows(g, mmax, rp.hq, rp.hkv, rp.d))
+           for _ in range(n_inputs)]
+    out = torch.empty((mmax, rp.hq, rp.d), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for t, (P, n) in enumerate(zip(starts, lengths), start=1):
+        m = n - P
+
+        def one_pass():
+            rp.st.kv_truncate(0, P)
+            for layer in range(rp.layers):
+                q, k, v = ins[layer % n_inputs]
+                rp.st.extend_attn(0, layer, q[:m], k[:m], v[:m], out[:m])
+
+        one_pass()
+        torch.cuda.synchronize()
+        rp.st.timing_start(passes * rp.layers)
+        for _ in range(passes):
+            one_pass()
+        kt = rp.st.timing_read()
+        c = kt["calls"]
+        attn = kt["attn_ms"] / c * 1e3
+        call = (kt["attn_ms"] + kt["append_ms"] + kt["combine_ms"]) / c * 1e3
+        tf = attn_flops(P, m, rp.hq, rp.d) / (attn * 1e-6) / 1e12
+        res[t] = {"cached": P, "new": m, "attn_us": r2(attn), "call_kernels_us": r2(call),
+                  "tok_per_s": round(m / (call * 1e-6), 1), "attn_TFLOPs": round(tf, 1),
+                  "attn_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
 # ---------------------------------------------------------------------------
 # measured HBM ceilings
 # ---------------------------------------------------------------------------
@@ -722,6 +765,13 @@ def main():
            "roofline": roofline}
 
     if not args.no_extra:
+        log("replay turns")
+        out["replay_turns"] = {
+            "workload": "every turn of the agent replay (7B-like attention, 28 q / 4 KV heads, "
+                        "D 128; turn t: L_(t-1) cached + L_t - L_(t-1) new rows), "
+                        f"{args.layers} layers rotated; per call: the summed kernel durations "
+                        "from HIP events (eager calls), attention FLOPs / attention kernel time",
+            "per_turn": replay_turns(rp)}
         log("hbm probe")
         out["hbm_probe"] = hbm_probe(backlog)
         log("gemv sweep")
