@@ -715,11 +715,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
         u32x2 w;
         w[0] = pack_f16x2(O[rt][dt][0] * f, O[rt][dt][1] * f);
         w[1] = pack_f16x2(O[rt][dt][2] * f, O[rt][dt][3] * f);
-        *reinterpret_cast<u32x2*>(sg.ws_o + wrow + 16 * dt + 4 * kb) = w;
+        // streaming stores: the partials are read once, by the combine
+        // kernel (1.0 us less here, 0.7 us more there, at turn 9)
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(sg.ws_o + wrow + 16 * dt + 4 * kb));
       }
       if (kb == 0)
-        *reinterpret_cast<f32x4*>(sg.ws_ml + (((size_t)split * m + qi) * Hq + qh) * 4) =
-            f32x4{mref[rt], l, ldexpf(1.f, ex), 0.f};
+        __builtin_nontemporal_store(
+            f32x4{mref[rt], l, ldexpf(1.f, ex), 0.f},
+            reinterpret_cast<f32x4*>(sg.ws_ml + (((size_t)split * m + qi) * Hq + qh) * 4));
     }
   }
 }
