@@ -140,6 +140,11 @@ __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
 // row-block workgroups of the last split that append the call's rows
 constexpr int kAppendBlocks = 4;
 
+// dwords per staged partial row (D/2 fp16 pairs + 4 of padding against bank
+// conflicts)
+template <int D>
+constexpr int kStageRow = D / 2 + 4;
+
 // ONE: the call has a single piece (its fields load without first finding
 // the piece, one scalar round trip less). QB: several questions about one
 // state, so a new row also masks the new rows of the other questions (kept
@@ -710,15 +715,23 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     } else {
       const float f = ldexpf(inv, -ex);
       const size_t wrow = ((size_t)split * m * Hq) * D + orow;
+      // The row's fp16 partial goes through this wave's own LDS rows (group
+      // 1's second buffer, unused after the merge; LDS operations of a wave
+      // complete in order), so that each lane stores 16 contiguous bytes and
+      // a row leaves as 64-byte runs rather than 8-byte pieces. Streaming
+      // stores: the partials are read once, by the combine kernel.
+      uint32_t* sr = reinterpret_cast<uint32_t*>(&lds[1][1][0][0]) + (gw * 16 + col) * kStageRow<D>;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x2 w;
         w[0] = pack_f16x2(O[rt][dt][0] * f, O[rt][dt][1] * f);
         w[1] = pack_f16x2(O[rt][dt][2] * f, O[rt][dt][3] * f);
-        // streaming stores: the partials are read once, by the combine
-        // kernel (1.0 us less here, 0.7 us more there, at turn 9)
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(sg.ws_o + wrow + 16 * dt + 4 * kb));
+        *reinterpret_cast<u32x2*>(sr + 8 * dt + 2 * kb) = w;
       }
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sr + 16 * c + 4 * kb),
+                                    reinterpret_cast<u32x4*>(sg.ws_o + wrow + 32 * c + 8 * kb));
       if (kb == 0)
         __builtin_nontemporal_store(
             f32x4{mref[rt], l, ldexpf(1.f, ex), 0.f},
