@@ -23,7 +23,6 @@ using namespace sve;
 
 namespace {
 
-constexpr int kMaxSplits = 16;        // workspace: kMaxSplits x max_rows rows
 constexpr int kMaxDecodeSplits = 64;
 constexpr size_t kAlign = 256;
 thread_local std::string g_err;
@@ -142,38 +141,70 @@ int hip_fail(const sve_ctx* c, hipError_t e, const char* what) {
 // workgroup is empty.
 int mfma_first_block(int X, int g) { return X > 0 ? (int)(((long long)g * X) / 128) : 0; }
 
-// Uniform layout (every key in the store): split s holds tiles
-// [s, s+1) * tps. Returns workgroups per KV head; *splits = the count.
-int mfma_head_blocks(const AttnSeg& sg, int g, int tps, int* splits) {
-  const int S = sg.m > 0 ? ((sg.P + sg.m - 1) / 64 + 1 + tps - 1) / tps : 0;
+// tiles the rows of a piece see: keys [0, P + m)
+int mfma_tiles(const AttnSeg& sg) { return sg.m > 0 ? (sg.P + sg.m - 1) / 64 + 1 : 0; }
+
+// Workgroups per KV head of a piece whose split s holds tiles [b[s], b[s+1]).
+int mfma_head_blocks(const AttnSeg& sg, int g, const int* b, int S) {
   int hb = 0;
-  for (int s = 0; s < S; ++s) hb += sg.row_blocks - mfma_first_block(64 * s * tps - sg.P, g);
-  if (splits) *splits = S;
+  for (int s = 0; s < S; ++s) hb += sg.row_blocks - mfma_first_block(64 * b[s] - sg.P, g);
   return hb;
 }
 
-// Cached/new layout (new keys read from the call's inputs): S1 pieces cut
-// the cached tiles [0, nt0) evenly, then pieces of tpn new tiles. A cached
-// tile runs in the staged loop, a new tile in the slower epilogue, so no
-// piece mixes the two. Returns workgroups per KV head; *splits = S1 + new
-// pieces.
-int mfma_head_blocks_cn(const AttnSeg& sg, int g, int S1, int tpn, int* splits) {
-  const int nt0 = sg.P / 64;
-  const int new_max = sg.m > 0 ? (sg.P + sg.m - 1) / 64 + 1 - nt0 : 0;
-  const int S2 = (new_max + tpn - 1) / tpn;
-  int hb = S1 * sg.row_blocks;
-  for (int n = 0; n < S2; ++n) hb += sg.row_blocks - mfma_first_block(64 * (nt0 + n * tpn) - sg.P, g);
-  if (splits) *splits = S1 + S2;
-  return hb;
+// Uniform layout: split s holds tiles [s, s+1) * tps. Returns the split count.
+int bounds_uniform(const AttnSeg& sg, int tps, int* b) {
+  const int T = mfma_tiles(sg), S = (T + tps - 1) / tps;
+  for (int s = 0; s <= S; ++s) b[s] = std::min(s * tps, T);
+  return S;
 }
 
-// Estimated time (us) of one workgroup's piece, fitted to per-workgroup
-// timestamps of the turn-9 shapes: 5.8 fixed (arguments, query loads, the
-// merge and partial stores), 1.3 per cached tile in the staged loop, 4.0 +
-// 1.6 per new tile in the epilogue (its first round waits for the call's
-// rows).
+// Cached/new layout: S1 pieces cut the cached tiles [0, nt0) evenly, then
+// pieces of tpn tiles hold the tiles from nt0 on (the new keys).
+int bounds_cn(const AttnSeg& sg, int nt0, int S1, int tpn, int* b) {
+  const int T = mfma_tiles(sg);
+  nt0 = std::min(std::max(nt0, 0), T);
+  S1 = nt0 > 0 ? std::max(1, std::min(S1, nt0)) : 0;
+  int S = 0;
+  for (int s = 0; s < S1; ++s) b[S++] = s * nt0 / S1;
+  for (int t = nt0; t < T && S < kMaxSplits + 1; t += tpn) b[S++] = t;
+  b[std::min(S, kMaxSplits)] = T;
+  return S;
+}
+
+// Estimated time (us), from the kernel's start, of the slowest workgroup of
+// a piece with `cached` tiles in the staged loop and `fresh` tiles in the
+// new-key epilogue, fitted to per-workgroup timestamps of the replay's turn
+// 9: arguments, query loads and the first tile, then 0.85 per tile (the two
+// key groups share them), the epilogue's first round (which waits for the
+// call's rows) and its later tiles, the merge and the partial stores. A
+// piece of new tiles only skips the staged loop's first wait.
 double mfma_piece_us(int cached, int fresh) {
-  return 5.8 + 1.3 * cached + (fresh > 0 ? 4.0 + 1.6 * fresh : 0.0);
+  if (cached == 0) return 7.4 + 1.6 * fresh;
+  return 8.9 + 0.85 * cached + (fresh > 0 ? 2.55 + 1.4 * (fresh - 1) : 0.0);
+}
+
+// cost of a piece of tiles [a, e) when tiles from nt0 on are new (nt0 < 0:
+// every tile is in the store)
+double mfma_span_us(int a, int e, int nt0) {
+  const int cached = nt0 < 0 ? e - a : std::max(0, std::min(e, nt0) - a);
+  return mfma_piece_us(cached, e - a - cached);
+}
+
+// Balanced layout: from the first tile on, each piece takes tiles while its
+// estimated time stays within tau (at least one tile). Returns the split
+// count, kMaxSplits + 1 if more pieces would be needed.
+int bounds_balanced(const AttnSeg& sg, int nt0, double tau, int* b) {
+  const int T = mfma_tiles(sg);
+  int S = 0, t = 0;
+  while (t < T) {
+    if (S == kMaxSplits) return kMaxSplits + 1;
+    b[S++] = t;
+    int e = t + 1;
+    while (e < T && mfma_span_us(t, e + 1, nt0) <= tau) ++e;
+    t = e;
+  }
+  b[S] = T;
+  return S;
 }
 
 void plan_mfma(sve_ctx* c, AttnParams& p) {
@@ -184,93 +215,120 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
   // kernel itself (unsplit pieces)
   const bool fused = env_int("SVE_FUSED_APPEND", 1) != 0;
   const int forced = env_int("SVE_KV_SPLIT", 0);
-  // SVE_ATTN_LAYOUT: 0 chooses, 1 forces the uniform layout, 2 the
-  // cached/new one (where the new rows come from the inputs)
-  const int layout = env_int("SVE_ATTN_LAYOUT", 0);
-  bool cn_ok = forced <= 0;
-  for (int s = 0; s < p.nseg; ++s) cn_ok &= (fused || p.seg[s].nq > 1);
-  // uniform layout: the fewest tiles per split that keep the grid within one
-  // round of workgroups
-  int tps = 1, S1 = 0, tpn = 1;
-  long long uniform_blocks = 0;
-  {
-    int tmax = 1;
+  // SVE_ATTN_LAYOUT: 0 chooses (below), 1 the uniform layout, 2 the
+  // cached/new one, 3 balanced pieces
+  const int layout = forced > 0 ? 1 : env_int("SVE_ATTN_LAYOUT", 0);
+  int nt0[kMaxSeg];
+  for (int s = 0; s < p.nseg; ++s)  // questions read their rows from the inputs
+    nt0[s] = (fused || p.seg[s].nq > 1) ? p.seg[s].P / 64 : -1;
+  int bnd[kMaxSeg][kMaxSplits + 1];
+  int S[kMaxSeg];
+  auto blocks_of = [&]() {
+    long long wg = 0;
+    for (int s = 0; s < p.nseg; ++s) wg += (long long)p.Hkv * mfma_head_blocks(p.seg[s], g, bnd[s], S[s]);
+    return wg;
+  };
+  auto worst_of = [&]() {
+    double w = 0;
     for (int s = 0; s < p.nseg; ++s)
-      if (p.seg[s].m > 0) tmax = std::max(tmax, (p.seg[s].P + p.seg[s].m - 1) / 64 + 1);
-    tps = std::max(1, (tmax + kMaxSplits - 1) / kMaxSplits);
-    if (forced > 0) tps = std::max(tps, (tmax + forced - 1) / forced);
-    for (;; ++tps) {
-      uniform_blocks = 0;
-      for (int s = 0; s < p.nseg; ++s)
-        uniform_blocks += (long long)p.Hkv * mfma_head_blocks(p.seg[s], g, tps, nullptr);
-      if (forced > 0 || uniform_blocks <= kTarget || tps >= tmax) break;
-    }
+      for (int n = 0; n < S[s]; ++n) w = std::max(w, mfma_span_us(bnd[s][n], bnd[s][n + 1], nt0[s]));
+    return w;
+  };
+  int tmax = 1;
+  for (int s = 0; s < p.nseg; ++s) tmax = std::max(tmax, mfma_tiles(p.seg[s]));
+  // uniform layout: the fewest tiles per split that keep the grid within
+  // one round (one unsplit piece when even that needs more)
+  int tps = std::max(1, (tmax + kMaxSplits - 1) / kMaxSplits);
+  if (forced > 0) tps = std::max(tps, (tmax + forced - 1) / forced);
+  for (;; ++tps) {
+    for (int s = 0; s < p.nseg; ++s) S[s] = bounds_uniform(p.seg[s], tps, bnd[s]);
+    if (forced > 0 || blocks_of() <= kTarget || tps >= tmax) break;
   }
-  // cached/new layout where the uniform one needs more than one round (a
-  // long suffix over a short prefix): measured per-workgroup times show a
-  // piece mixing cached and new tiles costs less than the piece model below
-  // says, so the uniform layout stays where it fits
-  const bool cn = cn_ok && layout != 1 && (layout == 2 || uniform_blocks > kTarget);
-  if (cn) {
-    // the (S1, tpn) with the least estimated time: the slowest piece times
-    // the rounds of workgroups the grid needs
-    int new_max = 1, nt0_max = 0;
-    for (int s = 0; s < p.nseg; ++s) {
-      const AttnSeg& sg = p.seg[s];
-      if (sg.m <= 0) continue;
-      nt0_max = std::max(nt0_max, sg.P / 64);
-      new_max = std::max(new_max, (sg.P + sg.m - 1) / 64 + 1 - sg.P / 64);
-    }
+  int max_splits = 0;
+  for (int s = 0; s < p.nseg; ++s) max_splits = std::max(max_splits, S[s]);
+  // Choice (measured on the replay's turns): balanced pieces where the
+  // uniform split has long pieces (turn 9, 7 tiles: 0.5 us faster per call);
+  // the uniform split where its pieces are short (turns 2-8, 2-4 tiles:
+  // balanced pieces were 0.5-1.2 us slower, the piece model misjudging
+  // them) and where one unsplit piece already fills a round (the 1668-row
+  // prefill: no combine, 75 us against 79 us for split pieces + combine).
+  constexpr int kBalancedMinTiles = 5;
+  const bool balanced =
+      layout == 3 || (layout == 0 && max_splits > 1 && tps >= kBalancedMinTiles);
+  if (layout == 1 || (layout == 0 && !balanced)) {
+    // (the uniform tables above)
+  } else if (layout == 2) {
+    // the (S1, tpn) with the least estimated time
     double best = 1e30;
-    long long best_wg = 0;
-    for (int a = (nt0_max > 0 ? 1 : 0); a <= std::min(nt0_max, kMaxSplits - 1); ++a)
-      for (int b = 1; b <= new_max; ++b) {
-        long long wg = 0;
-        double worst = 0;
+    int bS1 = 1, btpn = 1;
+    for (int a = 1; a < kMaxSplits; ++a)
+      for (int tpn = 1; tpn <= tmax; ++tpn) {
         bool ok = true;
         for (int s = 0; s < p.nseg && ok; ++s) {
-          const AttnSeg& sg = p.seg[s];
-          if (sg.m <= 0) continue;
-          const int nt0 = sg.P / 64, s1 = nt0 > 0 ? std::min(a, nt0) : 0;
-          int S = 0;
-          wg += (long long)p.Hkv * mfma_head_blocks_cn(sg, g, s1, b, &S);
-          ok = S <= kMaxSplits;
-          const int nm = (sg.P + sg.m - 1) / 64 + 1 - nt0;
-          if (s1 > 0) worst = std::max(worst, mfma_piece_us((nt0 + s1 - 1) / s1, 0));
-          worst = std::max(worst, mfma_piece_us(0, std::min(b, nm)));
+          S[s] = bounds_cn(p.seg[s], nt0[s] < 0 ? mfma_tiles(p.seg[s]) : nt0[s], a, tpn, bnd[s]);
+          ok = S[s] <= kMaxSplits;
         }
         if (!ok) continue;
-        const double est = worst * (double)((wg + kTarget - 1) / kTarget);
-        if (est < best - 1e-9 || (est < best + 1e-9 && wg < best_wg)) {
+        const double est = worst_of() * (double)((blocks_of() + kTarget - 1) / kTarget);
+        if (est < best - 1e-9) {
           best = est;
-          best_wg = wg;
-          S1 = a;
-          tpn = b;
+          bS1 = a;
+          btpn = tpn;
         }
       }
-    S1 = env_int("SVE_STAGE_PIECES", S1);
-    tpn = std::max(1, env_int("SVE_NEW_TILES_PER_PIECE", tpn));
+    for (int s = 0; s < p.nseg; ++s)
+      S[s] = bounds_cn(p.seg[s], nt0[s] < 0 ? mfma_tiles(p.seg[s]) : nt0[s], bS1, btpn, bnd[s]);
+  } else {
+    // Balanced pieces: for r rounds of workgroups, the smallest per-piece
+    // time tau whose pieces fit r rounds (bisection: a larger tau makes
+    // fewer, longer pieces); estimated time = the slowest piece x r.
+    auto build = [&](double tau) {
+      for (int s = 0; s < p.nseg; ++s) {
+        S[s] = bounds_balanced(p.seg[s], nt0[s], tau, bnd[s]);
+        if (S[s] > kMaxSplits) return false;
+      }
+      return true;
+    };
+    double hi = 0;
+    for (int s = 0; s < p.nseg; ++s) hi = std::max(hi, mfma_span_us(0, mfma_tiles(p.seg[s]), nt0[s]));
+    double best = 1e30, best_tau = hi;
+    long long best_wg = 0;
+    for (int r = 1; r <= 4; ++r) {
+      auto fits = [&](double tau) { return build(tau) && blocks_of() <= (long long)r * kTarget; };
+      if (!fits(hi)) continue;
+      double lo = 0.0, h = hi;
+      for (int it = 0; it < 30; ++it) {
+        const double mid = 0.5 * (lo + h);
+        if (fits(mid))
+          h = mid;
+        else
+          lo = mid;
+      }
+      build(h);
+      const long long wg = blocks_of();
+      const double est = worst_of() * (double)((wg + kTarget - 1) / kTarget);
+      if (est < best - 1e-9 || (est < best + 1e-9 && wg < best_wg)) {
+        best = est;
+        best_tau = h;
+        best_wg = wg;
+      }
+    }
+    if (!build(best_tau)) {  // (cannot happen: one piece per call always fits)
+      for (int s = 0; s < p.nseg; ++s) S[s] = bounds_uniform(p.seg[s], tmax, bnd[s]);
+    }
   }
   long long ws_rows = 0;
   int blocks = 0, rows = 0, app = 0;
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
-    int S = 0;
-    const bool fz = fused || sg.nq > 1;  // questions read their rows from the inputs
-    sg.new_tile0 = fz ? sg.P / 64 : -1;
-    if (cn) {
-      const int nt0 = sg.P / 64;
-      sg.stage_pieces = nt0 > 0 ? std::max(1, std::min(S1, nt0)) : 0;
-      sg.new_tpp = tpn;
-      sg.head_blocks = mfma_head_blocks_cn(sg, g, sg.stage_pieces, tpn, &S);
-      sg.split_keys = 64;  // (unused by this layout)
-    } else {
-      sg.stage_pieces = -1;
-      sg.new_tpp = 1;
-      sg.head_blocks = mfma_head_blocks(sg, g, tps, &S);
-      sg.split_keys = 64 * tps;
-    }
-    sg.splits = std::max(S, 1);
+    sg.new_tile0 = nt0[s];
+    sg.tiled = 1;
+    sg.splits = std::max(S[s], 1);
+    for (int n = 0; n <= kMaxSplits; ++n)
+      sg.tile_bound[n] = n <= S[s] ? bnd[s][n] : bnd[s][S[s]];
+    if (S[s] == 0) sg.tile_bound[1] = 0;
+    sg.head_blocks = mfma_head_blocks(sg, g, bnd[s], S[s]);
+    sg.split_keys = 64;  // (the tile table holds the splits)
     sg.tail_split = 0;
     sg.append_begin = app;
     sg.append_blocks = fused && sg.nq <= 1 && sg.splits > 1 && sg.m > 0
@@ -289,10 +347,13 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
   p.total_rows = rows;
   p.append_total = app;
   if (log_on()) {
-    fprintf(stderr, "[sve] extend: path=mfma pieces=%d blocks=%d layout=%s S1=%d tpn=%d tps=%d append=%d",
-            p.nseg, blocks, cn ? "cached/new" : "uniform", S1, tpn, tps, app);
-    for (int s = 0; s < p.nseg; ++s)
-      fprintf(stderr, " (P=%d m=%d splits=%d)", p.seg[s].P, p.seg[s].m, p.seg[s].splits);
+    fprintf(stderr, "[sve] extend: path=mfma pieces=%d blocks=%d layout=%s append=%d", p.nseg,
+            blocks, layout == 2 ? "cached/new" : balanced ? "balanced" : "uniform", app);
+    for (int s = 0; s < p.nseg; ++s) {
+      fprintf(stderr, " (P=%d m=%d tiles", p.seg[s].P, p.seg[s].m);
+      for (int n = 0; n <= S[s]; ++n) fprintf(stderr, " %d", bnd[s][n]);
+      fprintf(stderr, ")");
+    }
     fprintf(stderr, "\n");
   }
 }
@@ -370,8 +431,7 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     sg.tail_split = dec ? 1 : 0;
     sg.new_tile0 = -1;
     sg.head_blocks = sg.row_blocks * S;
-    sg.stage_pieces = -1;  // uniform splits (the combine's range rule)
-    sg.new_tpp = 1;
+    sg.tiled = 0;  // splits of split_keys keys (the combine's range rule)
     sg.append_blocks = sg.append_begin = 0;
     sg.block_begin = blocks;
     sg.row_begin = rows;

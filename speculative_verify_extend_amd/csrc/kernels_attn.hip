@@ -168,28 +168,23 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
   // from the first one whose last row sees a key of the split's tiles (the
   // first such block: g * X / (64 RT) for the split's first key P + X)
   const int kvh = ref.local / sg.head_blocks;
-  const int nt0s = sg.new_tile0, S1 = sg.stage_pieces, tpn = sg.new_tpp;
   int split = 0, rb = 0, t_lo = 0, t_hi = 0;
   {
+    // (unrolled over the table so its entries load together)
     int j = ref.local - kvh * sg.head_blocks;
-    if (S1 >= 0 && j < S1 * sg.row_blocks) {  // a piece of the cached tiles
-      split = j / sg.row_blocks;
-      rb = j - split * sg.row_blocks;
-      t_lo = split * nt0s / S1;
-      t_hi = (split + 1) * nt0s / S1;
-    } else {
-      const int tps = S1 >= 0 ? tpn : sg.split_keys / 64;
-      const int tbase = S1 >= 0 ? nt0s : 0;
-      if (S1 >= 0) j -= S1 * sg.row_blocks;
-      for (int n = 0; n < sg.splits; ++n) {
-        const int X = 64 * (tbase + n * tps) - P;
+    bool found = false;
+#pragma unroll
+    for (int n = 0; n < kMaxSplits; ++n) {
+      if (!found && n < sg.splits) {
+        const int lo = sg.tile_bound[n];
+        const int X = 64 * lo - P;
         const int rb0 = X > 0 ? (g * X) / (64 * RT) : 0;
         if (j < sg.row_blocks - rb0) {
-          split = (S1 >= 0 ? S1 : 0) + n;
+          found = true;
+          split = n;
           rb = rb0 + j;
-          t_lo = tbase + n * tps;
-          t_hi = t_lo + tps;
-          break;
+          t_lo = lo;
+          t_hi = sg.tile_bound[n + 1];
         }
         j -= sg.row_blocks - rb0;
       }
@@ -1349,15 +1344,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int c4 = (lane % CH) * 4, part = lane / CH;
   const int i = grow - sg.row_begin;
-  // uniform splits: those starting at or before the row's last key; the
-  // decode layout (cached splits + one new-key split): all of them
-  // (cached pieces and new-tile pieces: every cached piece, then the new
-  // pieces starting at or before the row's last tile)
-  const int nvalid =
-      sg.tail_split ? sg.splits
-      : sg.stage_pieces >= 0
-          ? min(sg.splits, sg.stage_pieces + ((sg.P + i) / 64 - sg.new_tile0) / sg.new_tpp + 1)
-          : min(sg.splits, (sg.P + i) / sg.split_keys + 1);
+  // the splits that hold a key the row sees: the decode layout (cached
+  // splits + one new-key split): all of them; otherwise those starting at or
+  // before the row's last key
+  int nvalid;
+  if (sg.tail_split) {
+    nvalid = sg.splits;
+  } else if (sg.tiled) {
+    // the splits whose first tile is at or before the row's last one
+    const int lt = (sg.P + i) / 64;
+    nvalid = 0;
+#pragma unroll
+    for (int n = 0; n < kMaxSplits; ++n) nvalid += (n < sg.splits) & (sg.tile_bound[n] <= lt);
+  } else {
+    nvalid = min(sg.splits, (sg.P + i) / sg.split_keys + 1);
+  }
   const float* mlp = sg.ws_ml + ((size_t)i * p.Hq + h) * 4;
   const uint16_t* op = sg.ws_o + ((size_t)i * p.Hq + h) * D + c4;
   const size_t ml_stride = (size_t)sg.m * p.Hq * 4, o_stride = (size_t)sg.m * p.Hq * D;

@@ -25,6 +25,7 @@ hipError_t launch_w4_gemv_routed(const void* x, int x_per_slot, int m, const int
 
 // ---- attention ------------------------------------------------------------------
 constexpr int kMaxSeg = 4;
+constexpr int kMaxSplits = 16;  // key splits per piece (workspace: kMaxSplits x max_rows rows)
 constexpr int kMaxQuestions = 16;
 
 // One (slot, layer) piece of an extend call. The KV store of a slot and layer
@@ -46,15 +47,14 @@ struct AttnSeg {
   int row_blocks;      // per KV head
   int splits, split_keys;
   int tail_split;      // decode layout: splits-1 cached splits of split_keys, then [P, P+m)
-  // MFMA path: head_blocks workgroups per KV head, split-major; a row block
-  // has a workgroup for a split only when one of its rows sees a key there.
-  // stage_pieces < 0: split s holds the 64-key tiles [s, s+1) * split_keys
-  // / 64 of every key. stage_pieces >= 0 (new keys read from the inputs):
-  // splits 0 .. stage_pieces-1 cut the cached tiles [0, new_tile0) evenly
-  // (split s: [s * nt0 / S1, (s+1) * nt0 / S1)), and split stage_pieces + n
-  // holds the new tiles [nt0 + n * new_tpp, nt0 + (n+1) * new_tpp).
+  // MFMA path (tiled = 1): head_blocks workgroups per KV head, split-major;
+  // split s holds the 64-key tiles [tile_bound[s], tile_bound[s+1]) (key
+  // [64t, 64t+64) is tile t), and a row block has a workgroup for a split
+  // only when one of its rows sees a key there. tiled = 0 (other paths):
+  // split s holds the keys [s, s+1) * split_keys.
   int head_blocks;
-  int stage_pieces, new_tpp;
+  int tiled;
+  int tile_bound[kMaxSplits + 1];
   // MFMA path: first 64-key tile [64t, 64t+64) that holds new keys (P / 64).
   // With new_tile0 >= 0 the attention kernel reads keys at or past P from
   // nk/nv (tiles from new_tile0 on); the rows are appended by the combine
