@@ -981,10 +981,10 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
   issue_w(ws0, q0);
   issue_w(ws1, q0 + 1);
   issue_w(ws2, q0 + 2);
-  f16x8 x1[4], x2[4];
-  load_x(4 * q0, x1);
-  load_x(4 * q0 + 1, x2);
-  wait_vmem<8>();  // the three weight quads are in
+  f16x8 xr[kGemmXAhead][4];  // activation groups in flight, oldest first
+#pragma unroll
+  for (int i = 0; i < kGemmXAhead; ++i) load_x(4 * q0 + i, xr[i]);
+  wait_vmem<4 * kGemmXAhead>();  // the three weight quads are in
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   dequant(ws0, bq0);
@@ -1015,10 +1015,11 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
         f16x8 xa[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          xa[a] = x1[a];
-          x1[a] = x2[a];
+          xa[a] = xr[0][a];
+#pragma unroll
+          for (int i = 0; i + 1 < kGemmXAhead; ++i) xr[i][a] = xr[i + 1][a];
         }
-        load_x(4 * q + j + kGemmXAhead, x2);
+        load_x(4 * q + j + kGemmXAhead, xr[kGemmXAhead - 1]);
         if (!live) continue;
         f16x8 bf[4];
 #pragma unroll
