@@ -363,6 +363,67 @@ def test_batched_split_and_unsplit_pieces_append():
         row += ms[i]
 
 
+@pytest.mark.parametrize("layout", [1, 2, 3], ids=["uniform", "cached-new", "balanced"])
+@pytest.mark.parametrize("case", [(28, 4, 128, 1668, 254), (28, 4, 128, 727, 134),
+                                  (4, 1, 64, 1000, 90), (8, 2, 128, 64, 300),
+                                  (8, 2, 128, 0, 400)],
+                         ids=lambda c: "h%d-%d-d%d-P%d-m%d" % c)
+def test_each_split_layout_matches_oracle(case, layout):
+    """The MFMA path's split tables filled each way (even tiles per split,
+    cached tiles then pieces of new tiles, balanced pieces): every row
+    matches the oracle and the appended rows are in the store, bit for bit.
+    Full-size rows are sampled to keep the oracle fast."""
+    hq, hkv, d, P, m = case
+    announce(f"split layout {layout} {case}")
+    c = synth.attention_case(17, hq, hkv, d, P, m)
+    st = _store(hq, hkv, d, P + m + 64, max(P, m, 1))
+    assert st.kv_slot_select(np.arange(P + m, dtype=np.int32)) == (0, 0)
+    if P:
+        st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]),
+                       dev_bf16(c["v_prefix"]))
+    with env(SVE_ATTN_LAYOUT=layout, SVE_MFMA_MIN_ROWS=1):
+        got = host_f64_of_bf16(st.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]),
+                                              dev_bf16(c["v"])))
+    kc = np.concatenate([c["k_prefix"], c["k"]])
+    vc = np.concatenate([c["v_prefix"], c["v"]])
+    rows = np.unique(np.concatenate([np.arange(0, m, max(1, m // 40)), [m - 1]]))
+    want = np.stack([extend_attention(c["q"][i:i + 1], kc[:P + i + 1], vc[:P + i + 1], P + i)[0]
+                     for i in rows])
+    assert np.abs(got[rows] - want).max() <= ATTN_TOL
+    kk, vv = st.kv_read(0, 0, 0, P + m)
+    assert np.array_equal(host_bits(kk), kc) and np.array_equal(host_bits(vv), vc)
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3], ids=["uniform", "cached-new", "balanced"])
+def test_each_split_layout_batched(layout):
+    """Several pieces in one launch share one choice of table filling."""
+    hq, hkv, d = 32, 8, 128
+    Ps, ms = [0, 500, 130], [60, 30, 100]
+    st = sve.KVSlots(3, 1, hq, hkv, d, 1024, 1024)
+    cases = [synth.attention_case(70 + i, hq, hkv, d, Ps[i], ms[i]) for i in range(3)]
+    announce(f"batched split layout {layout}")
+    for i in range(3):
+        toks = np.concatenate([[i + 1], np.arange(Ps[i] + ms[i] - 1)]).astype(np.int32)
+        assert st.kv_slot_select(toks) == (i, 0)
+        if Ps[i]:
+            st.extend_attn(i, 0, dev_bf16(cases[i]["q_prefix"]),
+                           dev_bf16(cases[i]["k_prefix"]), dev_bf16(cases[i]["v_prefix"]))
+    q = dev_bf16(np.concatenate([c["q"] for c in cases]))
+    k = dev_bf16(np.concatenate([c["k"] for c in cases]))
+    v = dev_bf16(np.concatenate([c["v"] for c in cases]))
+    with env(SVE_ATTN_LAYOUT=layout):
+        out = host_f64_of_bf16(st.extend_attn_batched([0, 1, 2], ms, 0, q, k, v))
+    row = 0
+    for i, c in enumerate(cases):
+        kc = np.concatenate([c["k_prefix"], c["k"]])
+        vc = np.concatenate([c["v_prefix"], c["v"]])
+        want = extend_attention(c["q"], kc, vc, Ps[i])
+        assert np.abs(out[row:row + ms[i]] - want).max() <= ATTN_TOL
+        kk, vv = st.kv_read(i, 0, 0, Ps[i] + ms[i])
+        assert np.array_equal(host_bits(kk), kc) and np.array_equal(host_bits(vv), vc)
+        row += ms[i]
+
+
 def test_kernel_timing_records_each_call():
     """Timing events around the three kernels of each timed call: positive
     attention time, a count capped at the requested calls, state errors,
