@@ -424,6 +424,60 @@ def test_each_split_layout_batched(layout):
         row += ms[i]
 
 
+def test_edges_empty_pieces_full_capacity_and_max_rows():
+    """A batched call whose pieces include empty ones; an extend that fills a
+    slot to its capacity (the last tile full, rows up to the arena's end);
+    exactly max_rows rows in one call, and one more refused."""
+    hq, hkv, d, cap = 28, 4, 128, 640
+    announce("edges: empty pieces, full capacity, max rows")
+    Ps, ms = [200, 0, 130, 64], [0, 177, 0, 63]
+    st = sve.KVSlots(4, 1, hq, hkv, d, cap, 240)
+    cases = [synth.attention_case(90 + i, hq, hkv, d, Ps[i], ms[i]) for i in range(4)]
+    for i in range(4):
+        toks = np.concatenate([[i + 1], np.arange(Ps[i] + max(ms[i], 1) - 1)]).astype(np.int32)
+        assert st.kv_slot_select(toks) == (i, 0)
+        if Ps[i]:
+            st.extend_attn(i, 0, dev_bf16(cases[i]["q_prefix"]), dev_bf16(cases[i]["k_prefix"]),
+                           dev_bf16(cases[i]["v_prefix"]))
+    q = dev_bf16(np.concatenate([c["q"] for c in cases]))
+    k = dev_bf16(np.concatenate([c["k"] for c in cases]))
+    v = dev_bf16(np.concatenate([c["v"] for c in cases]))
+    out = host_f64_of_bf16(st.extend_attn_batched([0, 1, 2, 3], ms, 0, q, k, v))
+    row = 0
+    for i, c in enumerate(cases):
+        if ms[i]:
+            want = extend_attention(c["q"], np.concatenate([c["k_prefix"], c["k"]]),
+                                    np.concatenate([c["v_prefix"], c["v"]]), Ps[i])
+            assert np.abs(out[row:row + ms[i]] - want).max() <= ATTN_TOL, i
+        assert st.kv_len(i, 0) == Ps[i] + ms[i]
+        row += ms[i]
+
+    # a slot filled to its capacity: 400 cached rows + 240 (= max_rows) new
+    P, m = cap - 240, 240
+    c = synth.attention_case(95, hq, hkv, d, P, m)
+    st2 = sve.KVSlots(1, 1, hq, hkv, d, cap, 400)
+    assert st2.kv_slot_select(np.arange(cap, dtype=np.int32)) == (0, 0)
+    st2.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]), dev_bf16(c["v_prefix"]))
+    got = host_f64_of_bf16(st2.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]),
+                                           dev_bf16(c["v"])))
+    kc = np.concatenate([c["k_prefix"], c["k"]])
+    vc = np.concatenate([c["v_prefix"], c["v"]])
+    want = extend_attention(c["q"], kc, vc, P)
+    assert np.abs(got - want).max() <= ATTN_TOL
+    kk, vv = st2.kv_read(0, 0, 0, cap)
+    assert np.array_equal(host_bits(kk), kc) and np.array_equal(host_bits(vv), vc)
+
+    # max_rows: 240 rows in one call pass (above), 241 are refused
+    st3 = sve.KVSlots(1, 1, hq, hkv, d, cap, 240)
+    assert st3.kv_slot_select(np.arange(300, dtype=np.int32)) == (0, 0)
+    q3, k3, v3 = (dev_bf16(a) for a in synth.attention_rows(synth.rng(96), 241, hq, hkv, d))
+    with pytest.raises(sve.SveError):
+        st3.extend_attn(0, 0, q3, k3, v3)
+    assert st3.kv_len(0, 0) == 0
+    st3.extend_attn(0, 0, q3[:240], k3[:240], v3[:240])
+    assert st3.kv_len(0, 0) == 240
+
+
 def test_kernel_timing_records_each_call():
     """Timing events around the three kernels of each timed call: positive
     attention time, a count capped at the requested calls, state errors,
