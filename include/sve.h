@@ -127,6 +127,11 @@ int sve_info(const sve_ctx* ctx, int32_t* granted_slots, int32_t* capacity);
  *   new_v: device bf16 [m][Hkv][D]
  *   out:   device bf16 [m][Hq][D]    (fp32 accumulation, rounded to nearest even)
  * m == 0 is a no-op. Asynchronous; the cached length becomes P+m.
+ * The call enqueues kernel launches only (no memset or copy), so it can be
+ * captured in a HIP graph. The checks, the launch plan and the cached length
+ * are host work done when the call is made: a replay repeats the same
+ * positions and inputs, so it is valid after the same cut back and select
+ * as at capture.
  * Errors: SVE_E_SLOT, SVE_E_ARG, SVE_E_CAPACITY (m > max_rows),
  * SVE_E_STATE (P+m beyond the prompt committed by the last select), SVE_E_HIP. */
 int sve_extend_attn(sve_ctx* ctx, int32_t slot, int32_t layer, const void* q, const void* new_k,
