@@ -72,6 +72,24 @@ def test_questions_under_forced_splits(splits):
     assert np.abs(host_f64_of_bf16(out) - want).max() <= ATTN_TOL
 
 
+@pytest.mark.parametrize("layout", [1, 2, 3], ids=["uniform", "cached-new", "balanced"])
+@pytest.mark.parametrize("case", [(28, 4, 128, 1668, [100, 90, 64]), (8, 2, 128, 0, [200, 150]),
+                                  (4, 2, 64, 500, [33, 1, 96])],
+                         ids=lambda c: "h%d-%d-d%d-P%d-q%d" % (c[:4] + (len(c[4]),)))
+def test_questions_under_each_split_layout(case, layout):
+    """Questions whose bands cross the split boundaries of every table
+    filling (a question's rows and keys spread over several pieces)."""
+    hq, hkv, d, prefix, ms = case
+    announce(f"questions layout={layout} {case}")
+    c, st = _state(hq, hkv, d, prefix, ms, seed=71)
+    with env(SVE_ATTN_LAYOUT=layout):
+        out = st.extend_attn_questions(0, 0, ms, dev_bf16(c["q"]), dev_bf16(c["k"]),
+                                       dev_bf16(c["v"]))
+    want = extend_attention_questions(c["q"], c["k_prefix"], c["v_prefix"], c["k"], c["v"], ms)
+    assert np.abs(host_f64_of_bf16(out) - want).max() <= ATTN_TOL
+    assert st.kv_len(0, 0) == prefix
+
+
 def test_questions_equal_separate_extends():
     """One call with four questions against four extends of the prefix, each
     cut back to the prefix afterwards (the previous way: the prefix is read
