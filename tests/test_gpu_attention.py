@@ -366,7 +366,8 @@ def test_batched_split_and_unsplit_pieces_append():
 @pytest.mark.parametrize("layout", [1, 2, 3], ids=["uniform", "cached-new", "balanced"])
 @pytest.mark.parametrize("case", [(28, 4, 128, 1668, 254), (28, 4, 128, 727, 134),
                                   (4, 1, 64, 1000, 90), (8, 2, 128, 64, 300),
-                                  (8, 2, 128, 0, 400)],
+                                  (8, 2, 128, 0, 400), (16, 16, 64, 900, 200),
+                                  (32, 4, 128, 1500, 300)],
                          ids=lambda c: "h%d-%d-d%d-P%d-m%d" % c)
 def test_each_split_layout_matches_oracle(case, layout):
     """The MFMA path's split tables filled each way (even tiles per split,
