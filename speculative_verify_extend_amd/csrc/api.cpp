@@ -207,7 +207,7 @@ int bounds_balanced(const AttnSeg& sg, int nt0, double tau, int* b) {
   return S;
 }
 
-void plan_mfma(sve_ctx* c, AttnParams& p) {
+int plan_mfma(sve_ctx* c, AttnParams& p) {
   constexpr int kTarget = 256;  // one workgroup per CU (128 KB of LDS each)
   const int g = p.g;
   // the attention kernel reads the new rows from the call's inputs; they
@@ -220,7 +220,7 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
   const int layout = forced > 0 ? 1 : env_int("SVE_ATTN_LAYOUT", 0);
   int nt0[kMaxSeg];
   for (int s = 0; s < p.nseg; ++s)  // questions read their rows from the inputs
-    nt0[s] = (fused || p.seg[s].nq > 1) ? p.seg[s].P / 64 : -1;
+    nt0[s] = (fused || p.seg[s].no_append) ? p.seg[s].P / 64 : -1;
   int bnd[kMaxSeg][kMaxSplits + 1];
   int S[kMaxSeg];
   auto blocks_of = [&]() {
@@ -331,7 +331,7 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
     sg.split_keys = 64;  // (the tile table holds the splits)
     sg.tail_split = 0;
     sg.append_begin = app;
-    sg.append_blocks = fused && sg.nq <= 1 && sg.splits > 1 && sg.m > 0
+    sg.append_blocks = fused && !sg.no_append && sg.splits > 1 && sg.m > 0
                            ? p.Hkv * ((sg.P + sg.m - 1) / 64 - sg.P / 64 + 1) * (p.D / 32)
                            : 0;
     app += sg.append_blocks;
@@ -346,6 +346,8 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
   p.total_blocks = blocks;
   p.total_rows = rows;
   p.append_total = app;
+  if (ws_rows > (long long)kMaxSplits * c->cfg.max_rows)
+    return fail(c, SVE_E_CAPACITY, "split workspace too small for this call");
   if (log_on()) {
     fprintf(stderr, "[sve] extend: path=mfma pieces=%d blocks=%d layout=%s append=%d", p.nseg,
             blocks, layout == 2 ? "cached/new" : balanced ? "balanced" : "uniform", app);
@@ -356,6 +358,7 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
     }
     fprintf(stderr, "\n");
   }
+  return SVE_OK;
 }
 
 // Choose the path, row blocks and key splits of every piece of a call.
@@ -366,7 +369,7 @@ void plan_mfma(sve_ctx* c, AttnParams& p) {
 //   valu:   kept for comparison (SVE_MFMA_MIN_ROWS / SVE_ATTN_PATH select it)
 // Splits: as many as keep the grid near one round of workgroups, within 64
 // per piece and within the split workspace (16 x max_rows rows in total).
-void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
+int plan_attention(sve_ctx* c, AttnParams& p, int& path) {
   const int g = p.g;
   int max_m = 0, max_r = 0;
   for (int s = 0; s < p.nseg; ++s) {
@@ -391,29 +394,33 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     p.seg[s].row_blocks = (p.seg[s].m * g + rpb - 1) / rpb;
     base += p.Hkv * p.seg[s].row_blocks;
   }
-  if (path == kPathMfma) {
-    plan_mfma(c, p);
-    return;
-  }
+  if (path == kPathMfma) return plan_mfma(c, p);
   const int target = path == kPathValu ? 512 : 256;
   const int unit = path == kPathDecode ? 128 : 64;  // split length granule (keys)
   const int max_splits = path == kPathDecode ? kMaxDecodeSplits : kMaxSplits;
   const int forced = env_int("SVE_KV_SPLIT", 0);
   const long long ws_cap = (long long)kMaxSplits * c->cfg.max_rows;  // workspace rows
+  const bool dec = path == kPathDecode;
+  // fewest splits a piece can take: a decode piece with cached keys has at
+  // least one cached split and the new-key split
+  auto min_splits = [&](const AttnSeg& sg) { return dec && sg.P > 0 ? 2 : 1; };
   long long ws_rows = 0;
   int blocks = 0, rows = 0;
   for (int s = 0; s < p.nseg; ++s) {
     AttnSeg& sg = p.seg[s];
-    const bool dec = path == kPathDecode;
     // decode: the cached keys [0, P) are split, and one more split holds
     // the new keys; other paths split all P + m keys uniformly
     const int keys = dec ? sg.P : sg.P + sg.m;
     // (whole rounds of workgroups: at most `target` workgroups in flight)
     int S = forced > 0 ? forced : target / std::max(base, 1);
     S = std::max(1, std::min(S, max_splits));
-    // the pieces after this one keep at least one split row each
-    const long long room = ws_cap - ws_rows - (p.total_rows_hint - rows - sg.m);
-    S = (int)std::max(1LL, std::min<long long>(S, room / std::max(sg.m, 1)));
+    // the pieces after this one keep the workspace rows of their fewest
+    // splits (the workspace holds kMaxSplits x max_rows rows, so the fewest
+    // splits of every piece always fit together)
+    long long later = 0;
+    for (int t = s + 1; t < p.nseg; ++t) later += (long long)min_splits(p.seg[t]) * p.seg[t].m;
+    const long long room = ws_cap - ws_rows - later;
+    S = (int)std::max<long long>(min_splits(sg), std::min<long long>(S, room / std::max(sg.m, 1)));
     if (dec) S = std::max(S - 1, 1);  // cached splits
     S = std::min(S, (keys + unit - 1) / unit);
     int sk = 0;
@@ -443,6 +450,7 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
   }
   p.total_blocks = blocks;
   p.total_rows = rows;
+  if (ws_rows > ws_cap) return fail(c, SVE_E_CAPACITY, "split workspace too small for this call");
   if (path == kPathDecode) {
     int max_sk = 0;
     for (int s = 0; s < p.nseg; ++s) max_sk = std::max(max_sk, p.seg[s].split_keys);
@@ -457,6 +465,7 @@ void plan_attention(sve_ctx* c, AttnParams& p, int& path) {
               p.seg[s].split_keys);
     fprintf(stderr, "\n");
   }
+  return SVE_OK;
 }
 
 int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int layer,
@@ -501,9 +510,8 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
     sg.m = ms[i];
     row += ms[i];
   }
-  p.total_rows_hint = total;
   int path = kPathMfma;
-  plan_attention(c, p, path);
+  if (const int rc = plan_attention(c, p, path)) return rc;
   hipEvent_t* ev = nullptr;
   uint8_t* ran = nullptr;
   if (c->timed_used < c->timed_max) {
@@ -570,9 +578,9 @@ int run_questions(sve_ctx* c, int slot, int layer, int nq, const int32_t* ms,
   sg.m = (int)total;
   sg.nq = nq;
   for (int j = 0, r = 0; j < nq; r += ms[j], ++j) sg.qstart[j] = r;
+  sg.no_append = 1;  // the slot is only read, whatever the number of questions
   sg.row_blocks = (sg.m * p.g + attn_rows_per_block(kPathMfma) - 1) / attn_rows_per_block(kPathMfma);
-  p.total_rows_hint = sg.m;
-  plan_mfma(c, p);
+  if (const int rc = plan_mfma(c, p)) return rc;
   hipError_t e = launch_attn(p, kPathMfma, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "questions attention launch");
   e = launch_attn_combine(p, c->stream);

@@ -72,7 +72,8 @@ constexpr int kAppendRows = 16;
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AttnParams p) {
   const AttnSeg& sg = p.seg[blockIdx.z];
-  if (sg.new_tile0 >= 0) return;  // the attention kernel appends this piece
+  // the attention kernel appends this piece, or nothing is appended
+  if (sg.new_tile0 >= 0 || sg.no_append) return;
   const int i0 = blockIdx.x * kAppendRows;
   if (i0 >= sg.m) return;
   const int h = blockIdx.y, Hkv = p.Hkv, cap = p.cap;
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
     // distinct banks) and leave as 16-byte pieces of 8 keys of one column,
     // key by key in the pieces holding P or P+m.
     const int A = min(sg.row_blocks, kAppendBlocks);
-    if (sg.splits == 1 && sg.nq <= 1 && rb < A) {
+    if (sg.splits == 1 && !sg.no_append && rb < A) {
       constexpr int VST = D + 2;
       uint16_t* Va = &lds[0][0][0][0];  // [64][VST]
       const uint16_t* nkh = sg.nk + (size_t)kvh * D;
@@ -853,10 +854,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams prm) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int key = kbase + 8 * (col >> 2) + 4 * sub + (col & 3);
-        // cached keys read the store (positions up to the next 32-key
-        // boundary exist and are masked); new keys read the call's rows
+        // cached keys read the store, new keys the call's rows; a key at or
+        // past the split's end (the last 32-key step of the last cached
+        // split when P % 32 != 0) reads the split's last row instead: its
+        // score is masked, and the store at or past P is never read (the
+        // new-key split writes there in this launch, and past P + m it
+        // holds whatever an earlier, cut-back extend left)
         const uint16_t* krow = tail ? nkh + (size_t)min(key - P, m - 1) * Hkv * D
-                                    : Kg + (size_t)key * D;
+                                    : Kg + (size_t)min(key, k1 - 1) * D;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
           kop[u][sub][dc] = as_bf16x8(load16(krow + 32 * dc + 8 * kb));
@@ -864,9 +869,28 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams prm) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 16 * dt + col;
-        vop[u][dt] = tail ? as_bf16x8(*reinterpret_cast<const u32x4*>(
-                                Vs + d * kDecMaxNew + 32 * sst + 8 * kb))
-                          : as_bf16x8(load16(Vg + (size_t)d * cap + kbase + 8 * kb));
+        if (tail) {
+          vop[u][dt] = as_bf16x8(
+              *reinterpret_cast<const u32x4*>(Vs + d * kDecMaxNew + 32 * sst + 8 * kb));
+        } else {
+          // the lane's 8 keys; value operands at or past the split's end are
+          // zero (a masked key has probability 0, and 0 times a stale
+          // non-finite value would still be NaN), and never read
+          const int c0 = kbase + 8 * kb;
+          const uint16_t* vrow = Vg + (size_t)d * cap;
+          if (c0 + 8 <= k1) {
+            vop[u][dt] = as_bf16x8(load16(vrow + c0));
+          } else {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t lo = c0 + 2 * e < k1 ? vrow[c0 + 2 * e] : 0u;
+              const uint32_t hi = c0 + 2 * e + 1 < k1 ? vrow[c0 + 2 * e + 1] : 0u;
+              w[e] = lo | (hi << 16);
+            }
+            vop[u][dt] = as_bf16x8(w);
+          }
+        }
       }
     }
 #pragma unroll

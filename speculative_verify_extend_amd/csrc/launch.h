@@ -68,6 +68,9 @@ struct AttnSeg {
   // the prefix [0, P) and the rows of its own question up to itself, and
   // nothing is appended. nq <= 1: an ordinary extend.
   int nq;
+  // 1: the call only reads the store (several questions, any nq): no kernel
+  // appends the piece's rows, and every key at or past P comes from nk/nv
+  int no_append;
   int qstart[kMaxQuestions];
   int block_begin;     // first linear workgroup of this piece
   int row_begin;       // first output row of this piece in a combined launch
@@ -82,7 +85,6 @@ struct AttnParams {
   int append_total;    // combine-kernel append workgroups (before the combine's own)
   float c;             // log2(e) / sqrt(D)
   int dec_rt, dec_ns;  // decode path: 16-row tiles per block (1, 2), steps per round (1, 2)
-  int total_rows_hint; // rows of the whole call (planning only)
 };
 
 enum AttnPath { kPathValu = 0, kPathMfma = 1, kPathDecode = 2 };
