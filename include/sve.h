@@ -264,6 +264,25 @@ int sve_verify_accept(const float* logits, int32_t m, int32_t V, const int32_t* 
                       int32_t* result, void* workspace, size_t workspace_bytes,
                       void* hip_stream);
 
+/* Allocation-free form of sve_verify_accept, for callers that cannot
+ * allocate device memory or hand the library a workspace (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, result and kernels, without the workspace: the partial
+ * results live in a static device array of the library (32 KB; every GPU it
+ * runs on holds one copy until the process ends), whose address is looked
+ * up once per GPU on the first call there with that GPU current (make that
+ * first call outside graph capture). The call allocates nothing.
+ *   1 <= m <= SVE_VERIFY_MAX_ROWS, 1 <= V <= SVE_VERIFY_NOALLOC_MAX_V; the
+ *   stream must belong to the current device.
+ * All calls on one GPU share the array and it keeps the last call's
+ * contents (nothing in it needs to start cleared): calls that overlap on one
+ * GPU, for instance on two streams, race and must be ordered by the caller.
+ * ASYNC on hip_stream. Errors: SVE_E_ARG (also V beyond the maximum),
+ * SVE_E_HIP. */
+#define SVE_VERIFY_NOALLOC_MAX_V 1048576
+int sve_verify_accept_noalloc(const float* logits, int32_t m, int32_t V, const int32_t* draft,
+                              int32_t* result, void* hip_stream);
+
 /* Rolling-acceptance gate of one request (host only). Each verify step
  * records its accepted count; the rolling acceptance is (sum of the last
  * `window` counts) / (k * those steps), fewer steps at the start; once it is

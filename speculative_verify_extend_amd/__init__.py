@@ -17,7 +17,8 @@ from ._lib import SveError, check
 
 __all__ = ["KVSlots", "ngram_draft", "w4_packed_bytes", "w4_pack", "w4_dequant", "w4_gemv_m", "w4_gemm",
            "w4_gemm_workspace_bytes",
-           "w4_gemv_m_routed", "verify_workspace_bytes", "verify_accept", "SpecGate",
+           "w4_gemv_m_routed", "verify_workspace_bytes", "verify_accept", "verify_accept_noalloc",
+           "SpecGate",
            "spec_break_even", "probe_read", "probe_copy", "SveError", "load_library"]
 
 
@@ -303,6 +304,23 @@ def verify_accept(logits: torch.Tensor, draft: torch.Tensor | None,
     check(lib.sve_verify_accept(_ptr(logits), m, vocab,
                                 None if draft is None else _ptr(draft), _ptr(result),
                                 _ptr(workspace), workspace.numel(), _stream()))
+    return result
+
+
+def verify_accept_noalloc(logits: torch.Tensor, draft: torch.Tensor | None,
+                          result: torch.Tensor) -> torch.Tensor:
+    """verify_accept without a workspace: the library keeps its partial
+    results in a static per-GPU array and allocates nothing (the caller
+    passes the result tensor). Calls that overlap on one GPU race."""
+    lib = _lib.load()
+    m, vocab = logits.shape
+    _need(logits, torch.float32, (m, vocab), "logits")
+    if m > 1 or draft is not None:
+        _need(draft, torch.int32, (m - 1,), "draft")
+    _need(result, torch.int32, (2 + m,), "result")
+    check(lib.sve_verify_accept_noalloc(_ptr(logits), m, vocab,
+                                        None if draft is None else _ptr(draft), _ptr(result),
+                                        _stream()))
     return result
 
 

@@ -37,6 +37,7 @@ class SveConfig(C.Structure):
 
 
 SVE_VERIFY_MAX_ROWS = 16
+SVE_VERIFY_NOALLOC_MAX_V = 1 << 20
 SVE_GATE_MAX_WINDOW = 64
 
 
@@ -81,6 +82,7 @@ _SIGS = {
     "sve_verify_workspace_bytes": (C.c_size_t, [_I, _I]),
     "sve_ngram_draft": (C.c_int, [_P, _I, _I, _I, _I, _P, C.POINTER(_I)]),
     "sve_verify_accept": (C.c_int, [_P, _I, _I, _P, _P, _P, C.c_size_t, _P]),
+    "sve_verify_accept_noalloc": (C.c_int, [_P, _I, _I, _P, _P, _P]),
     "sve_spec_gate_init": (C.c_int, [_P, _I, C.c_double, _I]),
     "sve_spec_gate_step": (C.c_int, [_P, _I, C.POINTER(_I)]),
     "sve_spec_break_even": (C.c_double, [C.c_double, C.c_double, _I]),

@@ -24,6 +24,7 @@ using namespace sve;
 namespace {
 
 constexpr int kMaxDecodeSplits = 64;
+static_assert(SVE_VERIFY_NOALLOC_MAX_V == kVerifyNoAllocMaxV, "header and kernels agree");
 constexpr size_t kAlign = 256;
 thread_local std::string g_err;
 
@@ -950,6 +951,17 @@ int sve_verify_accept(const float* logits, int32_t m, int32_t V, const int32_t* 
     return fail(nullptr, SVE_E_ARG, "workspace smaller than sve_verify_workspace_bytes");
   SVE_HIP(nullptr, launch_verify_accept(logits, m, V, draft, result, workspace,
                                         (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_verify_accept_noalloc(const float* logits, int32_t m, int32_t V, const int32_t* draft,
+                              int32_t* result, void* hip_stream) {
+  if (m < 1 || m > SVE_VERIFY_MAX_ROWS) return fail(nullptr, SVE_E_ARG, "m must be 1..16");
+  if (V < 1 || V > SVE_VERIFY_NOALLOC_MAX_V)
+    return fail(nullptr, SVE_E_ARG, "V must be 1..SVE_VERIFY_NOALLOC_MAX_V (static scratch size)");
+  if (!logits || !result || (m > 1 && !draft)) return fail(nullptr, SVE_E_ARG, "null pointer");
+  SVE_HIP(nullptr, launch_verify_accept_noalloc(logits, m, V, draft, result,
+                                                (hipStream_t)hip_stream));
   return SVE_OK;
 }
 

@@ -13,6 +13,7 @@
 // chunk results and one lane runs the acceptance scan. The order (value descending, index
 // ascending) is total, so the result does not depend on the reduction order.
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -115,6 +116,50 @@ size_t verify_workspace_bytes(int m, int V) {
   const size_t nchunk = ((size_t)V + kVerifyChunk - 1) / kVerifyChunk;
   const size_t half = ((size_t)m * nchunk * 4 + 255) / 256 * 256;
   return 2 * half;
+}
+
+// Scratch of the allocation-free entry point: the per-(row, chunk) partial
+// results of up to kVerifyMaxRows rows of kVerifyNoAllocMaxV logits (the
+// layout of verify_workspace_bytes). Every GPU the library runs on holds its
+// own copy until the process ends; every call on that GPU shares it, so
+// calls that overlap on one GPU race. Nothing in it has to start at zero:
+// the first kernel writes every (row, chunk) entry the second one reads.
+constexpr size_t kVerifyScratchBytes =
+    2 * (((size_t)kVerifyMaxRows * (kVerifyNoAllocMaxV / kVerifyChunk) * 4 + 255) / 256 * 256);
+static __device__ __align__(256) uint8_t scratch[kVerifyScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU
+}  // namespace
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current). In host code the array's name only stands in
+// for the symbol: kernels get the looked-up address.
+static hipError_t verify_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_verify_accept_noalloc(const float* logits, int m, int V, const int32_t* draft,
+                                        int32_t* result, hipStream_t st) {
+  if (verify_workspace_bytes(m, V) > kVerifyScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = verify_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_verify_accept(logits, m, V, draft, result, ws, st);
 }
 
 hipError_t launch_verify_accept(const float* logits, int m, int V, const int32_t* draft,

@@ -103,6 +103,11 @@ constexpr int kVerifyMaxRows = 16;
 size_t verify_workspace_bytes(int m, int V);
 hipError_t launch_verify_accept(const float* logits, int m, int V, const int32_t* draft,
                                 int32_t* result, void* workspace, hipStream_t st);
+// the same kernels over the library's static per-GPU scratch array (no
+// allocation, no workspace argument); V <= kVerifyNoAllocMaxV
+constexpr int kVerifyNoAllocMaxV = 1 << 20;
+hipError_t launch_verify_accept_noalloc(const float* logits, int m, int V, const int32_t* draft,
+                                        int32_t* result, hipStream_t st);
 
 // ---- measurement probes ------------------------------------------------------------
 hipError_t launch_probe_read(const void* src, size_t bytes, int blocks, int unroll, void* sink,

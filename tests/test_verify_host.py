@@ -62,3 +62,21 @@ def test_bad_gate_and_verify_arguments():
     assert lib.sve_verify_accept(p, 4, 0, p, p, p, ws, None) == _lib.SVE_E_ARG
     assert lib.sve_verify_accept(p, 4, 1000, None, p, p, ws, None) == _lib.SVE_E_ARG
     assert lib.sve_verify_accept(p, 4, 1000, p, p, p, ws - 1, None) == _lib.SVE_E_ARG
+
+
+def test_noalloc_verify_arguments_fail_before_gpu_work():
+    """The allocation-free verify form rejects sizes beyond its static scratch
+    (and the usual bad arguments) on the host, before any HIP call."""
+    lib = _lib.load()
+    p = C.c_void_p(256)
+    vmax = _lib.SVE_VERIFY_NOALLOC_MAX_V
+    assert lib.sve_verify_accept_noalloc(p, 4, vmax + 1, p, p, None) == _lib.SVE_E_ARG
+    assert b"static scratch" in lib.sve_last_error(None)
+    assert lib.sve_verify_accept_noalloc(p, 0, 100, p, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_verify_accept_noalloc(p, 17, 100, p, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_verify_accept_noalloc(p, 4, 0, p, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_verify_accept_noalloc(None, 4, 100, p, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_verify_accept_noalloc(p, 4, 100, None, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_verify_accept_noalloc(p, 4, 100, p, None, None) == _lib.SVE_E_ARG
+    # the largest vocabulary fits the scratch of the largest row count
+    assert lib.sve_verify_workspace_bytes(16, vmax) <= 32768
