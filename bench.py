@@ -182,6 +182,11 @@ def attn_bytes(P, m, hq, hkv, d):
     return 2 * (P + m) * hkv * d * 2 + 2 * m * hq * d * 2 + 4 * m * hkv * d * 2
 
 
+def exp_count(P, m, hq):
+    """Exponentials of an extend: one per visible (row, head, key) pair."""
+    return hq * (m * P + m * (m + 1) // 2)
+
+
 def gemv_bytes(m, n, k):
     return n * (k // 2) + n * (k // 32) * 2 + 2 * m * k + 4 * m * n
 
@@ -338,16 +343,62 @@ def replay_turns(rp, passes=2, n_inputs=4):
 # measured HBM ceilings
 # ---------------------------------------------------------------------------
 
-def hbm_probe(backlog):
-    """Plain streaming read (1 GiB) and copy (2 x 512 MiB) of device memory."""
+# read-probe launch shapes (mode, threads, blocks, loads in flight) that came
+# out best over a sweep of 152 shapes at 9-57 MB and 1 GiB on this chip
+# (mode 0: plain loads, 1: nontemporal loads, 2: direct global-to-LDS loads)
+READ_SHAPES = [(2, 1024, 512, 1), (2, 512, 256, 4), (2, 256, 512, 4), (2, 1024, 256, 8),
+               (0, 512, 1024, 8), (1, 512, 512, 2), (1, 1024, 256, 2), (1, 256, 256, 16)]
+
+
+def read_ceiling_us(bufs, backlog, shapes=READ_SHAPES, reps=2):
+    """Fastest plain read of same-sized buffers (rotated): the median
+    per-launch time (ms) of the best launch shape. At most 8 launches per
+    event bracket, so the host stays ahead of the GPU."""
+    lib, st = sve.load_library(), sve._stream()
+    best = math.inf
+    for mode, threads, blocks, unroll in shapes:
+        nb = bufs[0].numel() * bufs[0].element_size()
+        if mode == 2 and (nb % 1024 or nb >= (1 << 31)):
+            continue
+        sink = torch.empty(blocks * threads, dtype=torch.int32, device="cuda")
+        calls = [lambda p=sve._ptr(b), sp=sve._ptr(sink): lib.sve_probe_read(
+            p, nb, blocks, threads, unroll, mode, sp, st) for b in bufs]
+        d = []
+        for _ in range(reps):
+            for i in range(0, len(calls), 8):
+                d += bracket(calls[i:i + 8], backlog)
+        best = min(best, float(np.median(d)))
+    return best
+
+
+def ceilings(backlog):
+    """Measured ceilings of this chip beside the published peaks: HBM read
+    (1 GiB, best launch shape) and copy, bf16 / fp16 MFMA issue rate,
+    v_exp_f32 throughput and LDS read bandwidth (kernels in libsve's probe
+    file, HIP events per launch)."""
     buf = backlog.buf
-    read = min(bracket([lambda: sve.probe_read(buf, 1024, 1)] * 3, backlog))
+    read = read_ceiling_us([buf] * 3, backlog, reps=1)
     half = buf.numel() // 2
     src, dst = buf[:half], buf[half:]
     copy = min(bracket([lambda: sve.probe_copy(src, dst, 2048)] * 3, backlog))
-    return {"read_GBps": round(buf.numel() / (read * 1e-3) / 1e9, 1),
-            "copy_GBps": round(2 * half / (copy * 1e-3) / 1e9, 1),
-            "what": "streaming read of 1 GiB and copy of 512 MiB, HIP events per launch"}
+    out = {"hbm_read_GBps": round(buf.numel() / (read * 1e-3) / 1e9, 1),
+           "hbm_copy_GBps": round(2 * half / (copy * 1e-3) / 1e9, 1)}
+    blocks, iters = 2048, 2000
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    waves = blocks * 4
+    per_wave = {0: ("mfma_bf16_16x16x32_TFLOPs", 8 * 16384 / 1e12),
+                1: ("mfma_bf16_32x32x16_TFLOPs", 8 * 32768 / 1e12),
+                2: ("mfma_f16_16x16x32_TFLOPs", 8 * 16384 / 1e12),
+                3: ("v_exp_f32_T_per_s", 64 * 64 / 1e12),
+                4: ("lds_read_TBps", 8 * 1024 / 1e12)}
+    for kind, (name, per) in per_wave.items():
+        sve.probe_compute(kind, blocks, iters, sink)
+        ms = min(bracket([lambda k=kind: sve.probe_compute(k, blocks, iters, sink)] * 3, backlog))
+        out[name] = round(per * waves * iters / (ms * 1e-3), 2)
+    out["what"] = ("HBM: streaming read of 1 GiB (best of the read-probe launch shapes) and copy "
+                   "of 512 MiB; compute: 2048 workgroups x 4 waves x 2000 iterations of 8 matrix "
+                   "products, 64 exponentials or 8 wave-wide 16-byte LDS reads; HIP events")
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -368,15 +419,7 @@ def gemv_sweep(shapes, backlog, copies=8, m_values=range(1, 9), seed=3, reps=3):
         del wd, sd
     kmax = max(k for _, k in shapes)
     xs = [bf16_dev(synth.normal_bf16(g, (8, kmax))) for _ in range(copies)]
-    floors = {}
-    for (n, k, packs) in mats:
-        best = math.inf
-        for blocks, unroll in ((1024, 2), (2048, 2), (512, 4)):
-            d = []
-            for _ in range(reps):
-                d += bracket([lambda p=p: sve.probe_read(p, blocks, unroll) for p in packs], backlog)
-            best = min(best, float(np.median(d)))
-        floors[(n, k)] = best
+    floors = {(n, k): read_ceiling_us(packs, backlog) for (n, k, packs) in mats}
     res = {}
     for m in m_values:
         per = {}
@@ -693,6 +736,11 @@ def main():
         return
 
     backlog = Backlog()
+    log("ceilings")
+    for _ in range(200):  # clocks up before anything is timed
+        backlog()
+    torch.cuda.synchronize()
+    ceil = ceilings(backlog)
     log("replay setup")
     rp = Replay(args.layers)
     for _ in range(args.warmup):
@@ -746,7 +794,13 @@ def main():
                 "algorithmic_bytes_per_launch": attn_bytes(rp.P, rp.m, rp.hq, rp.hkv, rp.d),
                 "timing": "HIP events recorded by the library on its stream around the kernel, "
                           f"averaged over {calls} eager calls",
-                "other_kernels_us": {"kv_append": r2(append_us), "combine": r2(combine_us)}}
+                "other_kernels_us": {"kv_append": r2(append_us), "combine": r2(combine_us)},
+                "measured_peak": ceil["mfma_bf16_16x16x32_TFLOPs"],
+                "frac_of_measured": round(achieved / ceil["mfma_bf16_16x16x32_TFLOPs"], 4),
+                "measured_peak_what": "v_mfma_f32_16x16x32_bf16 (the kernel's instruction) issued "
+                                      "back to back on every SIMD (bench ceilings)",
+                "exp_bound_us": r2(exp_count(rp.P, rp.m, rp.hq) / (ceil["v_exp_f32_T_per_s"] * 1e12)
+                                   * 1e6)}
     if append_us == 0.0:
         roofline["other_kernels_us"]["kv_append"] = "none: the attention kernel appends the rows"
 
@@ -772,8 +826,7 @@ def main():
                         f"{args.layers} layers rotated; per call: the summed kernel durations "
                         "from HIP events (eager calls), attention FLOPs / attention kernel time",
             "per_turn": replay_turns(rp)}
-        log("hbm probe")
-        out["hbm_probe"] = hbm_probe(backlog)
+        out["ceilings"] = ceil
         log("gemv sweep")
         g9 = gemv_sweep(synth.layer_gemv_shapes(4096, 12288, 32, 8, 128), backlog)
         g7 = gemv_sweep(synth.layer_gemv_shapes(3584, 18944, 28, 4, 128), backlog, copies=6,
@@ -786,7 +839,11 @@ def main():
                         "time from HIP events; layer = sum of the four launches",
             "roofline": {"bound": "hbm", "achieved": round(worst, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(worst / HBM_PEAK_GBS, 4),
-                         "what": "worst m of 1..8, algorithmic bytes / summed kernel time"},
+                         "what": "worst m of 1..8, algorithmic bytes / summed kernel time",
+                         "frac_of_measured": round(min(v["floor_us"] / v["us"] for v in g9.values()), 4),
+                         "measured_what": "the same four launches' best plain read of the same "
+                                          "packed buffers (per-size ceiling: launch, ramp and tail "
+                                          "included) over the layer time, worst m"},
             "per_m": {m: {"us": r2(v["us"]), "GBps": round(v["GBps"], 1),
                           "frac": round(v["GBps"] / HBM_PEAK_GBS, 4),
                           "read_floor_us": r2(v["floor_us"]),

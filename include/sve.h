@@ -310,16 +310,36 @@ int sve_spec_gate_step(sve_spec_gate* gate, int32_t accepted, int32_t* k_next);
 double sve_spec_break_even(double a, double b, int32_t k);
 
 /* ---- measurement probes (not part of the computation) ---------------------
- * Plain streaming read and plain copy of device memory, used to measure the
- * achievable HBM bandwidth beside the published peak and to calibrate the
- * hardware traffic counters against a kernel that moves a known byte count.
- *   src, dst: device buffers of `bytes` bytes (a multiple of 16).
- *   blocks: workgroups of 256 threads (1..65536); unroll: loads in flight per
- *   thread (1, 2, 4 or 8); sink: device uint32 [blocks*256], written.
+ * The achievable ceilings of the chip beside its published peaks, and a
+ * kernel of known traffic that calibrates the hardware counters.
+ *
+ * Streaming read of `bytes` bytes of device memory at src (a multiple of
+ * 16): `blocks` workgroups of `threads` threads (a multiple of 64, at most
+ * 1024), grid-stride.
+ *   mode 0: each thread keeps `unroll` 16-byte loads in flight (1, 2, 4, 8 or
+ *           16) and folds them into one word: sink device uint32
+ *           [blocks * threads].
+ *   mode 1: the same with nontemporal loads.
+ *   mode 2: direct global-to-LDS loads, each wave a ring of `unroll` 1 KB
+ *           slots (bytes % 1024 == 0, bytes < 2 GiB, threads/64 * unroll KB
+ *           of LDS at most 160 KB): sink device uint32 [blocks].
+ * Plain copy: src to dst, `bytes` each (a multiple of 16), 256-thread blocks.
  * Errors: SVE_E_ARG, SVE_E_HIP. */
-int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll, void* sink,
-                   void* hip_stream);
+int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t threads,
+                   int32_t unroll, int32_t mode, void* sink, void* hip_stream);
 int sve_probe_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* hip_stream);
+
+/* Compute ceilings: `blocks` workgroups of 256 threads (4 waves) run `iters`
+ * iterations each. Per wave and iteration:
+ *   kind 0: 8 v_mfma_f32_16x16x32_bf16 (16384 flops each),
+ *   kind 1: 8 v_mfma_f32_32x32x16_bf16 (32768 flops each),
+ *   kind 2: 8 v_mfma_f32_16x16x32_f16  (16384 flops each),
+ *   kind 3: 64 v_exp_f32 of 64 lanes (eight independent chains),
+ *   kind 4: 8 LDS reads of 16 bytes per lane (1 KB per wave each).
+ * sink: device uint32 [blocks * 256], written. The rate is the count above
+ * times blocks * 4 * iters over the measured kernel time.
+ * Errors: SVE_E_ARG, SVE_E_HIP. */
+int sve_probe_compute(int32_t kind, int32_t blocks, int32_t iters, void* sink, void* hip_stream);
 
 /* ---- kernel timing (measurement aid) -------------------------------------
  * sve_timing_start makes the next n_calls extend calls on ctx record HIP

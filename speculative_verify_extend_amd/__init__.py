@@ -19,7 +19,7 @@ __all__ = ["KVSlots", "ngram_draft", "w4_packed_bytes", "w4_pack", "w4_dequant",
            "w4_gemm_workspace_bytes",
            "w4_gemv_m_routed", "verify_workspace_bytes", "verify_accept", "verify_accept_noalloc",
            "SpecGate",
-           "spec_break_even", "probe_read", "probe_copy", "SveError", "load_library"]
+           "spec_break_even", "probe_read", "probe_copy", "probe_compute", "SveError", "load_library"]
 
 
 def load_library():
@@ -347,13 +347,23 @@ def spec_break_even(a: float, b: float, k: int) -> float:
     return float(_lib.load().sve_spec_break_even(float(a), float(b), int(k)))
 
 
-def probe_read(src: torch.Tensor, blocks: int, unroll: int = 4) -> torch.Tensor:
-    """Streaming read of a device buffer (measurement probe)."""
-    if src.device.type != "cuda" or not src.is_contiguous():
-        raise ValueError("src must be a contiguous GPU tensor")
-    sink = torch.empty(blocks * 256, dtype=torch.int32, device=src.device)
-    check(_lib.load().sve_probe_read(_ptr(src), src.numel() * src.element_size(), blocks, unroll,
-                                     _ptr(sink), _stream()))
+def probe_read(src: torch.Tensor, blocks: int, unroll: int = 4, threads: int = 256,
+               mode: int = 0) -> torch.Tensor:
+    """Streaming read of a device buffer (measurement probe). mode 0: plain
+    loads, 1: nontemporal loads, 2: direct global-to-LDS loads."""
+    nbytes = src.numel() * src.element_size()
+    sink = torch.empty(blocks * (1 if mode == 2 else threads), dtype=torch.int32, device=src.device)
+    check(_lib.load().sve_probe_read(_ptr(src), nbytes, blocks, threads, unroll, mode, _ptr(sink),
+                                     _stream()))
+    return sink
+
+
+def probe_compute(kind: int, blocks: int, iters: int, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Compute-ceiling probe (kind 0: bf16 MFMA 16x16x32, 1: bf16 MFMA
+    32x32x16, 2: fp16 MFMA 16x16x32, 3: v_exp_f32, 4: LDS reads)."""
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    check(_lib.load().sve_probe_compute(kind, blocks, iters, _ptr(sink), _stream()))
     return sink
 
 

@@ -74,7 +74,8 @@ _SIGS = {
     "sve_w4_gemv_m_routed": (C.c_int, [_P, _I, _I, _P, _I, _P, _I, _I, _I, _P, _P]),
     "sve_w4_gemm_workspace_bytes": (C.c_size_t, [_I, _I, _I]),
     "sve_w4_gemm": (C.c_int, [_P, _I, _P, _I, _I, _P, _P, C.c_size_t, _P]),
-    "sve_probe_read": (C.c_int, [_P, C.c_size_t, _I, _I, _P, _P]),
+    "sve_probe_read": (C.c_int, [_P, C.c_size_t, _I, _I, _I, _I, _P, _P]),
+    "sve_probe_compute": (C.c_int, [_I, _I, _I, _P, _P]),
     "sve_probe_copy": (C.c_int, [_P, _P, C.c_size_t, _I, _P]),
     "sve_timing_start": (C.c_int, [_P, _I]),
     "sve_timing_read": (C.c_int, [_P, C.POINTER(C.c_float), C.POINTER(C.c_float),

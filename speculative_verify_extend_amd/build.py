@@ -33,6 +33,13 @@ COMMON_FLAGS = [
 ]
 
 
+# per-source extra flags. The compute probes keep MFMA accumulators in
+# ordinary vector registers: with the default (accumulation registers) the
+# compiler copies the eight 16x16 accumulators around the probe's loop, and
+# the probe would time the copies instead of the matrix cores.
+EXTRA_FLAGS = {"kernels_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -41,7 +48,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

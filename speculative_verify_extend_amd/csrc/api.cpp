@@ -536,8 +536,10 @@ int run_extend(sve_ctx* c, int n, const int32_t* slots, const int32_t* ms, int l
   e = launch_attn(p, path, c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "extend_attn launch");
   if (ev) SVE_HIP(c, hipEventRecord(ev[2], c->stream));
-  e = launch_attn_combine(p, c->stream);
-  if (e != hipSuccess) return hip_fail(c, e, "combine launch");
+  if (need_combine) {
+    e = launch_attn_combine(p, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "combine launch");
+  }
   if (ev) SVE_HIP(c, hipEventRecord(ev[3], c->stream));
   for (int i = 0; i < n; ++i) c->kv_len[slots[i]][layer] += ms[i];
   return SVE_OK;
@@ -1018,13 +1020,28 @@ double sve_spec_break_even(double a, double b, int32_t k) {
   return 0.5 * (lo + hi);
 }
 
-int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t unroll, void* sink,
-                   void* hip_stream) {
+int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t threads,
+                   int32_t unroll, int32_t mode, void* sink, void* hip_stream) {
   if (!src || !sink || bytes == 0 || bytes % 16) return fail(nullptr, SVE_E_ARG, "bad probe buffer");
   if (blocks < 1 || blocks > 65536) return fail(nullptr, SVE_E_ARG, "blocks must be 1..65536");
-  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
-    return fail(nullptr, SVE_E_ARG, "unroll must be 1, 2, 4 or 8");
-  SVE_HIP(nullptr, launch_probe_read(src, bytes, blocks, unroll, sink, (hipStream_t)hip_stream));
+  if (threads < 64 || threads > 1024 || threads % 64)
+    return fail(nullptr, SVE_E_ARG, "threads must be a multiple of 64 in 64..1024");
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
+    return fail(nullptr, SVE_E_ARG, "unroll must be 1, 2, 4, 8 or 16");
+  if (mode < 0 || mode > 2) return fail(nullptr, SVE_E_ARG, "mode must be 0, 1 or 2");
+  if (mode == 2 && (bytes % 1024 || bytes > 0x7FFFFFFFu ||
+                    (size_t)(threads / 64) * unroll * 1024 > 160 * 1024))
+    return fail(nullptr, SVE_E_ARG, "LDS mode: bytes % 1024 == 0, < 2 GiB, ring within 160 KB");
+  SVE_HIP(nullptr, launch_probe_read(src, bytes, blocks, threads, unroll, mode, sink,
+                                     (hipStream_t)hip_stream));
+  return SVE_OK;
+}
+
+int sve_probe_compute(int32_t kind, int32_t blocks, int32_t iters, void* sink, void* hip_stream) {
+  if (kind < 0 || kind > 4) return fail(nullptr, SVE_E_ARG, "kind must be 0..4");
+  if (blocks < 1 || blocks > 65536 || iters < 1) return fail(nullptr, SVE_E_ARG, "bad blocks or iters");
+  if (!sink) return fail(nullptr, SVE_E_ARG, "null sink");
+  SVE_HIP(nullptr, launch_probe_compute(kind, blocks, iters, sink, (hipStream_t)hip_stream));
   return SVE_OK;
 }
 

@@ -110,8 +110,12 @@ hipError_t launch_verify_accept_noalloc(const float* logits, int m, int V, const
                                         int32_t* result, hipStream_t st);
 
 // ---- measurement probes ------------------------------------------------------------
-hipError_t launch_probe_read(const void* src, size_t bytes, int blocks, int unroll, void* sink,
-                             hipStream_t st);
+// mode 0: plain loads, 1: nontemporal loads, 2: direct global-to-LDS loads
+hipError_t launch_probe_read(const void* src, size_t bytes, int blocks, int threads, int unroll,
+                             int mode, void* sink, hipStream_t st);
+// kind 0: MFMA 16x16x32 bf16, 1: MFMA 32x32x16 bf16, 2: MFMA 16x16x32 f16,
+// 3: v_exp_f32, 4: LDS reads of 16 bytes
+hipError_t launch_probe_compute(int kind, int blocks, int iters, void* sink, hipStream_t st);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t st);
 
 // ---- slot matcher ----------------------------------------------------------------

@@ -97,3 +97,28 @@ def test_null_context_is_rejected(lib):
     f, i = C.c_float(), C.c_int32()
     assert lib.sve_timing_read(None, C.byref(f), C.byref(f), C.byref(f), C.byref(i)) == _lib.SVE_E_ARG
     assert lib.sve_strerror(_lib.SVE_E_STATE) == b"call out of order"
+
+
+def test_probe_arguments_fail_before_gpu_work(lib):
+    """The measurement probes check their launch shapes on the host."""
+    p = C.c_void_p(4096)
+    ok = dict(bytes=1 << 20, blocks=256, threads=256, unroll=4, mode=0)
+
+    def read(**kw):
+        a = dict(ok, **kw)
+        return lib.sve_probe_read(p, a["bytes"], a["blocks"], a["threads"], a["unroll"], a["mode"],
+                                  p, None)
+
+    assert read(bytes=0) == _lib.SVE_E_ARG
+    assert read(bytes=1000) == _lib.SVE_E_ARG
+    assert read(blocks=0) == _lib.SVE_E_ARG
+    assert read(threads=100) == _lib.SVE_E_ARG
+    assert read(threads=2048) == _lib.SVE_E_ARG
+    assert read(unroll=3) == _lib.SVE_E_ARG
+    assert read(mode=3) == _lib.SVE_E_ARG
+    assert read(mode=2, bytes=(1 << 20) + 16) == _lib.SVE_E_ARG       # not whole 1 KB chunks
+    assert read(mode=2, threads=1024, unroll=16) == _lib.SVE_E_ARG    # 256 KB ring > 160 KB of LDS
+    assert lib.sve_probe_compute(5, 1, 1, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_probe_compute(0, 0, 1, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_probe_compute(0, 1, 0, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_probe_compute(0, 1, 1, None, None) == _lib.SVE_E_ARG
