@@ -2,7 +2,7 @@
 """Benchmark of the extend-prefill / m-row int4 GEMV hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
-                    [--no-graph] [--layers L] [--calibrate]
+                    [--no-graph] [--layers L] [--calibrate] [--only SECTION]
 
 Timed step (the headline): one turn of the agent-turn replay at turn 9 on a
 7B-like attention layer (28 q / 4 KV heads, head_dim 128): truncate the slot
@@ -716,6 +716,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time the headline from eager launches only (for counter runs)")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
+    ap.add_argument("--only", choices=["gemv", "verify", "moe", "gemm", "accept", "ceilings"],
+                    help="run one section alone and print its JSON (counter and trace runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the copy probe (256 MiB, three times): the known byte count "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -733,6 +735,25 @@ def main():
             sve.probe_copy(src, dst, 4096)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": src.numel(), "launches": 3}))
+        return
+
+    if args.only:
+        backlog = Backlog()
+        for _ in range(200):
+            backlog()
+        torch.cuda.synchronize()
+        sections = {
+            "gemv": lambda: gemv_sweep(synth.layer_gemv_shapes(4096, 12288, 32, 8, 128), backlog,
+                                       m_values=(1, 4, 8)),
+            "verify": lambda: verify_sweep(backlog, layers=min(args.layers, ROT_LAYERS)),
+            "moe": lambda: moe_sweep(backlog),
+            "gemm": lambda: prefill_gemm_sweep(synth.layer_gemv_shapes(3584, 18944, 28, 4, 128),
+                                               backlog),
+            "accept": lambda: verify_accept_sweep(backlog),
+            "ceilings": lambda: ceilings(backlog),
+        }
+        log(args.only)
+        print(json.dumps({args.only: sections[args.only]()}, default=float), flush=True)
         return
 
     backlog = Backlog()

@@ -190,7 +190,7 @@ int sve_w4_dequant(const void* packed, int32_t N, int32_t K, float* out, void* h
  * all m rows ([spec] opening section: verify rows share one read of the
  * weights, so extra rows are nearly free).
  *   x: device bf16 [m][K]; packed: sve_w4_pack output; y: device fp32 [m][N].
- *   1 <= m <= 16, N >= 1, K % 32 == 0.
+ *   1 <= m <= 16, N >= 1, K % 32 == 0, K <= 4194304.
  * Errors: SVE_E_ARG, SVE_E_HIP. */
 int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
                   void* hip_stream);
@@ -223,7 +223,7 @@ int sve_w4_gemm(const void* x, int32_t m, const void* packed, int32_t N, int32_t
  * distinct expert's weights are read once for all pairs routed to it.
  *   expert_ids: device int32 [m][topk]; packed_all: E packed weights of
  *   sve_w4_packed_bytes(N, K) bytes each, back to back; y: device fp32
- *   [m][topk][N]. 1 <= m <= 16, 1 <= topk <= 16. An id outside 0..E-1
+ *   [m][topk][N]. 1 <= m <= 16, 1 <= topk <= 16, K <= 4194304. An id outside 0..E-1
  *   yields NaN in that pair's output row.
  * Errors: SVE_E_ARG, SVE_E_HIP. */
 int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int32_t* expert_ids,

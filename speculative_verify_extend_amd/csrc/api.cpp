@@ -24,6 +24,8 @@ using namespace sve;
 namespace {
 
 constexpr int kMaxDecodeSplits = 64;
+// the GEMVs address x through 32-bit buffer offsets: 256 rows of K bf16
+constexpr int kMaxGemvK = 1 << 22;
 static_assert(SVE_VERIFY_NOALLOC_MAX_V == kVerifyNoAllocMaxV, "header and kernels agree");
 constexpr size_t kAlign = 256;
 thread_local std::string g_err;
@@ -873,7 +875,8 @@ int sve_w4_dequant(const void* packed, int32_t N, int32_t K, float* out, void* h
 int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32_t K, float* y,
                   void* hip_stream) {
   if (m < 1 || m > 16) return fail(nullptr, SVE_E_ARG, "m must be 1..16");
-  if (N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "need N >= 1 and K % 32 == 0");
+  if (N < 1 || K < 32 || K % 32 || K > kMaxGemvK)
+    return fail(nullptr, SVE_E_ARG, "need N >= 1, K % 32 == 0 and K <= 4194304");
   if (!x || !packed || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
   SVE_HIP(nullptr, launch_w4_gemv(x, m, packed, N, K, y, (hipStream_t)hip_stream,
                                   env_int("SVE_GEMV_WGS_PER_CU", 0)));
@@ -905,7 +908,8 @@ int sve_w4_gemv_m_routed(const void* x, int32_t x_per_slot, int32_t m, const int
   if (m < 1 || m > 16) return fail(nullptr, SVE_E_ARG, "m must be 1..16");
   if (topk < 1 || topk > 16) return fail(nullptr, SVE_E_ARG, "topk must be 1..16");
   if (x_per_slot != 0 && x_per_slot != 1) return fail(nullptr, SVE_E_ARG, "x_per_slot is 0 or 1");
-  if (E < 1 || N < 1 || K < 32 || K % 32) return fail(nullptr, SVE_E_ARG, "bad E, N or K");
+  if (E < 1 || N < 1 || K < 32 || K % 32 || K > kMaxGemvK)
+    return fail(nullptr, SVE_E_ARG, "bad E, N or K (K % 32 == 0, K <= 4194304)");
   if (!x || !ids || !packed_all || !y) return fail(nullptr, SVE_E_ARG, "null pointer");
   SVE_HIP(nullptr, launch_w4_gemv_routed(x, x_per_slot, m, ids, topk, packed_all, E, N, K, y,
                                          (hipStream_t)hip_stream));

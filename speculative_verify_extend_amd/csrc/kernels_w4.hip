@@ -372,9 +372,13 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kerne
   const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // activation operands (A row = input row r, rows past m repeat row m-1 and
-  // are never stored) and their C0 terms, once for the whole run
-  const uint16_t* xl = x + (size_t)min(r, m - 1) * K + 8 * kb;
+  // activation operands (A row = input row r) and their C0 terms, once for
+  // the whole run. Rows past m are never stored: their lanes read past the
+  // end of a buffer resource over x, which returns zeros without fetching,
+  // so only the m live rows cost address and cache bandwidth.
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, m * K * 2, kBufWord3);  // (m <= 16, K < 2^26)
+  const uint32_t xoff = r < m ? (uint32_t)(r * K + 8 * kb) * 2u : 0x80000000u;
   bf16x8 xa[QPW][4];
   f32x4 c0[HOIST ? QPW : 1][4];
 #pragma unroll
@@ -382,7 +386,8 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kerne
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int g = min(4 * (q0 + a) + j, G - 1);
-      xa[a][j] = as_bf16x8(load16(xl + 32 * g));
+      xa[a][j] = as_bf16x8(__builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 64u * g, 0, 0)));
     }
   // quads past K (the last wave of an uneven split re-reads a real block
   // there) meet zero activations, so they add exactly zero
@@ -499,9 +504,13 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
     const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
   __shared__ f32x4 part[kGemvMaxWaves * 64];
-  // per wave: one step's activations, [row][kLongStepK] bf16, rewritten
-  // every step (LDS operations of a wave complete in order)
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kLongMaxWaves][16 * kLongStepK];
+  // per wave: one step's activations, [row][kLongStepK] bf16 with rows
+  // kXRow elements apart, rewritten every step (LDS operations of a wave
+  // complete in order). The 16 extra bytes per row put the rows on
+  // different banks: with 512-byte rows every row of an operand read hit
+  // the same banks (8-way conflicts at m = 8).
+  constexpr int kXRow = kLongStepK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kLongMaxWaves][16 * kXRow];
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -550,14 +559,17 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (u < nu) store16(xw + 8 * (lane + 64 * u), b.xc[u]);
+      if (u < nu) {
+        const int e = lane + 64 * u;  // row e / 32, elements 8 * (e % 32) .. +7
+        store16(xw + (e >> 5) * kXRow + 8 * (e & 31), b.xc[u]);
+      }
 #pragma unroll
     for (int a = 0; a < kLongChunk; ++a) {
       const bool real = c * kLongChunk + a < nq;  // uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8 xa =
-            as_bf16x8(load16(xw + xr * kLongStepK + 128 * a + 32 * j + 8 * kb));
+            as_bf16x8(load16(xw + xr * kXRow + 128 * a + 32 * j + 8 * kb));
         const f32x4 c0 = mfma16x16x32(xa, neg136, zero4);
         const float sc = real ? scale_of(b.s[a], j) : 0.f;
         w4_group(xa, c0, b.w[a][j], sc, acc);
@@ -739,17 +751,24 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
         if (n < N) y[(size_t)rows[j] * N + n] = __builtin_nanf("");
       }
     } else {
-      // activations of the gathered pairs (rows past cnt repeat the last
-      // pair and are never stored); quads past K meet zero activations
+      // activations of the gathered pairs; rows past cnt are never stored
+      // and read past the end of a buffer resource over x (zeros, no
+      // fetch); quads past K meet zero activations
       const int pr = rows[min(r, cnt - 1)];
-      const uint16_t* xrow =
-          (x_per_slot ? x + (size_t)pr * K : x + (size_t)(pr / topk) * K) + 8 * kb;
+      const size_t xrows = x_per_slot ? (size_t)npairs : (size_t)m;
+      const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(x), (short)0, (int)(xrows * K * 2), kBufWord3);
+      const uint32_t xoff =
+          r < cnt ? (uint32_t)(((x_per_slot ? (size_t)pr : (size_t)(pr / topk)) * K + 8 * kb) * 2)
+                  : 0x80000000u;
       bf16x8 xa[QPW][4];
 #pragma unroll
       for (int a = 0; a < QPW; ++a)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          xa[a][j] = a < nq ? as_bf16x8(load16(xrow + 32 * min(4 * (q0 + a) + j, G - 1)))
+          xa[a][j] = a < nq ? as_bf16x8(__builtin_bit_cast(
+                                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             xrs, xoff + 64u * min(4 * (q0 + a) + j, G - 1), 0, 0)))
                             : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
       auto issue = [&](int t, TileBuf<QPW>& b) {
         t = min(t, t1 - 1);

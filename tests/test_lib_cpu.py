@@ -122,3 +122,14 @@ def test_probe_arguments_fail_before_gpu_work(lib):
     assert lib.sve_probe_compute(0, 0, 1, p, None) == _lib.SVE_E_ARG
     assert lib.sve_probe_compute(0, 1, 0, p, None) == _lib.SVE_E_ARG
     assert lib.sve_probe_compute(0, 1, 1, None, None) == _lib.SVE_E_ARG
+
+
+def test_gemv_shape_bounds_fail_before_gpu_work(lib):
+    """K beyond the 32-bit activation offsets, m out of range and bad K are
+    refused on the host."""
+    p = C.c_void_p(4096)
+    big = (1 << 22) + 32
+    assert lib.sve_w4_gemv_m(p, 1, p, 16, big, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemv_m(p, 17, p, 16, 64, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemv_m(p, 1, p, 16, 48, p, None) == _lib.SVE_E_ARG
+    assert lib.sve_w4_gemv_m_routed(p, 0, 1, p, 8, p, 4, 16, big, p, None) == _lib.SVE_E_ARG
