@@ -5,9 +5,10 @@
                     [--no-graph] [--layers L] [--calibrate] [--only SECTION]
 
 Timed step (the headline): one turn of the agent-turn replay at turn 9 on a
-7B-like attention layer (28 q / 4 KV heads, head_dim 128): truncate the slot
-back to the 1668 cached tokens, select the slot for the 1922-token prompt
-(reuses 1668), then extend 254 new rows in each of 128 attention layers. 128
+7B-like attention layer (28 q / 4 KV heads, head_dim 128): the slot is cut
+back to the 1668 cached tokens and selected for the 1922-token prompt (reuses
+1668) before the timed region, then 254 new rows are extended in each of 128
+attention layers (timed). 128
 layers are rotated so that the 500 MB of KV read per step cannot sit in the
 256 MB Infinity Cache. value = 254 new tokens per attention-layer pass / time
 of one pass (step time / 128), the per-layer calls replayed from a captured
@@ -672,16 +673,125 @@ def slots_rotation(backlog):
 
 
 # ---------------------------------------------------------------------------
+# the tiny single-layer configuration (cache-resident: a correctness config)
+# ---------------------------------------------------------------------------
+
+def tiny_config(backlog, reps=20):
+    """Tiny workload (4 q / 2 KV heads, D 64; 64 cached + 8 new rows; int4
+    weight 1024 x 256): the extend and the GEMV at m = 1..8, HIP events per
+    call. Everything fits in the caches, so these are latencies, not a
+    bandwidth measurement."""
+    wl = synth.WORKLOADS["tiny"]
+    hq, hkv, d, P, m = wl["hq"], wl["hkv"], wl["d"], wl["prefix"], wl["m"]
+    c = synth.attention_case(wl["seed"], hq, hkv, d, P, m)
+    st = sve.KVSlots(1, 1, hq, hkv, d, 256, 64)
+    st.kv_slot_select(np.arange(P + m, dtype=np.int32))
+    st.extend_attn(0, 0, bf16_dev(c["q_prefix"]), bf16_dev(c["k_prefix"]), bf16_dev(c["v_prefix"]))
+    q, k, v = bf16_dev(c["q"]), bf16_dev(c["k"]), bf16_dev(c["v"])
+    out = torch.empty_like(q)
+
+    def ext():
+        st.kv_truncate(0, P)
+        st.extend_attn(0, 0, q, k, v, out)
+    ext_us = float(np.median(bracket([ext] * reps, backlog))) * 1e3
+    n, kk = wl["gemv_n"], wl["gemv_k"]
+    w, s = synth.w4_weights(synth.rng(wl["seed"], 7), n, kk)
+    packed = sve.w4_pack(torch.from_numpy(w).cuda(), f16_dev(s), n, kk)
+    x = bf16_dev(synth.normal_bf16(synth.rng(wl["seed"], 8), (8, kk)))
+    gemv = {}
+    for mm in range(1, 9):
+        xm = x[:mm].contiguous()
+        y = torch.empty((mm, n), dtype=torch.float32, device="cuda")
+        gemv[mm] = r2(float(np.median(bracket([lambda: sve.w4_gemv_m(xm, packed, n, kk, y)] * reps,
+                                              backlog))) * 1e3)
+    st.close()
+    return {"workload": "tiny single layer: 4 q / 2 KV heads, D 64, 64 cached + 8 new rows; "
+                        "int4 weight 1024 x 256 (group 32)",
+            "cache_resident": True,
+            "extend_us": r2(ext_us), "gemv_us_per_m": gemv,
+            "note": "0.56 MFLOP and 49 KB of KV, 0.15 MB of weights: every operand is cache "
+                    "resident, so the times are launch and latency bound (a trivial kernel "
+                    "costs about 4.5 us between events on this chip)"}
+
+
+def gemv_content(backlog, m=8, copies=8, reps=3):
+    """The GEMV's time does not depend on the values it multiplies (the
+    weights are read once whatever the rows hold): the 9B-like layer at m
+    rows with x ~ N(0,1), x = 0, x = +-1e4, and with every weight code 8
+    (all-zero weights)."""
+    g = synth.rng(3, 57)
+    shapes = synth.layer_gemv_shapes(4096, 12288, 32, 8, 128)
+    layer = {}
+    for (n, k) in shapes:
+        w, sc = synth.w4_weights(g, n, k)
+        wd, sd = torch.from_numpy(w).cuda(), f16_dev(sc)
+        eights = torch.full_like(wd, 0x88)
+        layer[(n, k)] = ([sve.w4_pack(wd, sd, n, k) for _ in range(copies)],
+                         [sve.w4_pack(eights, sd, n, k) for _ in range(copies)])
+        del wd, sd, eights
+    kmax = max(k for _, k in shapes)
+    normal = synth.normal_bf16(g, (m, kmax))
+    big = synth.f32_to_bf16_bits(np.where(g.random((m, kmax)) < 0.5, -1e4, 1e4).astype(np.float32))
+    xs = {"normal": bf16_dev(normal), "zeros": torch.zeros((m, kmax), dtype=torch.bfloat16,
+                                                           device="cuda"),
+          "pm1e4": bf16_dev(big)}
+    variants = [(name, xt, 0) for name, xt in xs.items()] + [("codes_all_8", xs["normal"], 1)]
+    res = {}
+    for name, xt, which in variants:
+        tot = 0.0
+        for (n, k), packs2 in layer.items():
+            packs = packs2[which]
+            xk = xt[:, :k].contiguous()
+            ys = [torch.empty((m, n), dtype=torch.float32, device="cuda") for _ in range(copies)]
+            calls = [lambda c=c: sve.w4_gemv_m(xk, packs[c], n, k, ys[c]) for c in range(copies)]
+            for f in calls:
+                f()
+            d = []
+            for _ in range(reps):
+                d += bracket(calls, backlog)
+            tot += float(np.median(d)) * 1e3
+        res[name] = r2(tot)
+    vals = list(res.values())
+    return {"workload": f"9B-like layer GEMVs at m = {m}, 8 rotated weight copies; layer time "
+                        "(us) per content variant",
+            "layer_us": res, "spread": round(max(vals) / min(vals) - 1.0, 4)}
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(case, P, budget_s=10.0):
-    from oracle.attention import extend_attention
+def cpu_facts():
+    """CPU model, the cores this process may run on, and numpy's BLAS
+    (vendor, threads it uses)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    blas, threads = "unknown", affinity
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = "%s %s" % (infos[0].get("internal_api", "?"), infos[0].get("version", ""))
+            threads = max(i.get("num_threads", 1) for i in infos)
     except Exception:
-        threads = os.cpu_count() or 1
+        pass
+    return model, affinity, blas.strip(), threads
+
+
+def cpu_baseline(case, P, budget_s=10.0):
+    from oracle.attention import extend_attention
+    model, affinity, blas, threads = cpu_facts()
     k_all = np.concatenate([case["k_prefix"], case["k"]])
     v_all = np.concatenate([case["v_prefix"], case["v"]])
     n, t0 = 0, time.perf_counter()
@@ -694,7 +804,10 @@ def cpu_baseline(case, P, budget_s=10.0):
     m = case["q"].shape[0]
     return dict(value=m / dt, unit="tok/s", cores=int(threads), kind="oracle",
                 sample=f"turn 9 of the replay, one 7B-like attention layer (1668 cached + {m} "
-                       f"new rows, fp64 numpy), repeated {n}x over {budget_s:.0f} s")
+                       f"new rows, fp64 numpy), repeated {n}x over {budget_s:.0f} s",
+                cpu_model=model, affinity_cores=int(affinity), blas=blas,
+                cores_what="BLAS threads numpy used (the host's thread limit); affinity_cores "
+                           "= CPUs this process may run on")
 
 
 def log(msg):
@@ -716,7 +829,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time the headline from eager launches only (for counter runs)")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
-    ap.add_argument("--only", choices=["gemv", "verify", "moe", "gemm", "accept", "ceilings"],
+    ap.add_argument("--only", choices=["gemv", "verify", "moe", "gemm", "accept", "ceilings",
+                                       "tiny", "content"],
                     help="run one section alone and print its JSON (counter and trace runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the copy probe (256 MiB, three times): the known byte count "
@@ -751,6 +865,8 @@ def main():
                                                backlog),
             "accept": lambda: verify_accept_sweep(backlog),
             "ceilings": lambda: ceilings(backlog),
+            "tiny": lambda: tiny_config(backlog),
+            "content": lambda: gemv_content(backlog),
         }
         log(args.only)
         print(json.dumps({args.only: sections[args.only]()}, default=float), flush=True)
@@ -829,8 +945,9 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": "agent-turn replay turn 9: select + extend of 254 new rows over "
-                                  "1668 cached, 7B-like attention layer (28 q / 4 KV heads, D 128), "
+           "config": {"workload": "agent-turn replay turn 9: extend of 254 new rows over 1668 "
+                                  "cached (the slot is cut back and selected before the timed "
+                                  "region), 7B-like attention layer (28 q / 4 KV heads, D 128), "
                                   f"{args.layers} layers rotated, per-layer calls "
                                   + ("launched eagerly" if args.no_graph else
                                      "replayed from a captured HIP graph")
@@ -919,6 +1036,16 @@ def main():
             out["verify_attention"]["forced_" + path + "_attn_kernel_us"] = {
                 m: r2(v["attn_kernel_us"]) for m, v in vp.items()}
         os.environ.pop("SVE_MFMA_MIN_ROWS", None)
+        # one layer of a verify step: its four GEMVs plus the attention call
+        # (thinkspread's verify(m) = fixed + per-row cost, per layer here)
+        step = {m: g9[m]["us"] + vs[m]["call_us"] for m in range(1, 9)}
+        a4, b4 = fit(list(step), list(step.values()))
+        out["verify_step"] = {
+            "workload": "one 9B-like layer of a verify step: the four int4 GEMVs (QKV, O, "
+                        "gate|up, down) + the attention call over 2048 cached + m rows",
+            "per_m_us": {m: r2(v) for m, v in step.items()},
+            "fit_us": {"fixed": round(a4, 3), "per_row": round(b4, 3),
+                       "per_row_over_fixed": round(b4 / a4, 4)}}
         log("verify accept")
         va = verify_accept_sweep(backlog)
         out["verify_accept"] = {
@@ -940,6 +1067,10 @@ def main():
             "fit_us": {"fixed": round(a3, 3), "per_row": round(b3, 3)}}
         log("slots")
         out["slots"] = slots_rotation(backlog)
+        log("tiny")
+        out["tiny"] = tiny_config(backlog)
+        log("gemv content")
+        out["gemv_content"] = gemv_content(backlog)
 
     if not args.no_cpu:
         log("cpu baseline")
