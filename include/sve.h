@@ -21,6 +21,7 @@
  *   [spec]     thinkspread, "The economics of speculative decoding: +41% on
  *              9B, break-even on 35B"
  *   [quant]    thinkspread, "Models and quantizations"
+ *   [openjev]  openjev-multimodal, "Latency"
  */
 #ifndef SVE_H
 #define SVE_H
@@ -201,9 +202,12 @@ int sve_w4_gemv_m(const void* x, int32_t m, const void* packed, int32_t N, int32
  * the group-32 blocks are used in place). Same result definition as
  * sve_w4_gemv_m, for any number of rows: y[r][n] = sum_k x[r][k] * w[n][k],
  * w = (code - 8) * scale. It multiplies fp16 operands and accumulates in
- * fp32: each weight is (code - 8) * scale rounded once to fp16 (relative
- * error at most 2^-11) and x is converted to fp16 (exact for |x| < 65504;
- * larger values become infinite).
+ * fp32: each weight is (code - 8) * scale rounded once to fp16 and x is
+ * converted from bf16 to fp16. Both conversions are exact or within a
+ * relative 2^-11 in fp16's normal range (2^-14 <= |v| < 65504; a bf16 value
+ * there is exact); below 2^-14 the error is at most half an fp16 subnormal
+ * step (2^-25) and below 2^-25 values become 0; at 65520 and beyond they
+ * become infinite.
  *   x: device bf16 [m][K]; packed: sve_w4_pack output; y: device fp32 [m][N];
  *   workspace: device memory of at least sve_w4_gemm_workspace_bytes(m, N,
  *   K) bytes, owned by the caller and used only during the call's kernels
@@ -358,9 +362,10 @@ int sve_timing_start(sve_ctx* ctx, int32_t n_calls);
 int sve_timing_read(sve_ctx* ctx, float* append_ms, float* attn_ms, float* combine_ms,
                     int32_t* calls);
 
-/* ---- prompt-lookup drafting ([goinfer] "What we got wrong": with n-gram
- * speculation the runtime guesses the next tokens from text already in the
- * prompt and checks them in one verify step) ----------------------------------
+/* ---- prompt-lookup drafting ([goinfer] "What we got wrong": n-gram
+ * speculation drafts by copying what followed an earlier occurrence of the
+ * latest tokens in the prompt itself; one verify pass then accepts or rejects
+ * the draft) -------------------------------------------------------------------
  * Host-only integer search. For suffix lengths g = min(max_ngram, n-1) down
  * to min_ngram, finds the latest earlier start p (p = n-g-1 down to 0;
  * overlapping the suffix is allowed) with tokens[p..p+g) equal to the last

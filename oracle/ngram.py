@@ -3,8 +3,9 @@
 Test infrastructure only (see ``oracle/__init__.py``).
 
 goinfer, "Turn nine in under half a second", section "What we got wrong":
-with speculative decoding by n-grams the runtime guesses the next few tokens
-from text already in the prompt and checks them in one verify step.
+the n-gram form of speculation drafts its tokens by copying what followed an
+earlier occurrence of the latest tokens in the prompt itself, and a single
+verify pass then accepts or rejects the draft.
 
 Readings (the page says no more):
   * the guess continues the most recent earlier occurrence of the longest

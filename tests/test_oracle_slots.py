@@ -63,6 +63,41 @@ def test_exhaustive_small_cases():
     assert count > 10000
 
 
+def test_sampled_four_slot_cases():
+    """20,000 random states of four slots whose contents have length 0..5
+    over {0,1,2} (a third of them sharing a random common start), each with
+    a random prompt of length 1..5: the same properties as the exhaustive
+    test, for both rules."""
+    g = np.random.default_rng(11)
+    for i in range(20000):
+        base = g.integers(0, 3, size=5)
+        slots = []
+        for _ in range(4):
+            n = int(g.integers(0, 6))
+            t = g.integers(0, 3, size=n)
+            if i % 3 == 0 and n:
+                k = int(g.integers(0, n + 1))
+                t[:k] = base[:k]
+            slots.append(t)
+        p = g.integers(0, 3, size=int(g.integers(1, 6)))
+        literal = bool(i & 1)
+        o = SlotOracle(4, literal_rule=literal)
+        for s, t in enumerate(slots):
+            if len(t):
+                o.tokens[s] = t.copy()
+                o.kv_len[s] = [len(t)]
+                o.committed[s] = len(t)
+        before = [o.resident(s).copy() for s in range(4)]
+        el = o.eligible(p)
+        assert len(el) <= 1
+        if literal:
+            ua = unique_argmax_rule(p, [x if len(x) else None for x in before])
+            assert (el[0] if el else None) == ua
+        s, r = o.select(p)
+        assert 0 <= r <= len(p) - 1
+        assert np.array_equal(before[s][:r], p[:r])
+
+
 def test_reuse_off_never_reuses():
     o = SlotOracle(4, reuse=False)
     for _, p in synth.rotation_sessions(1, 2, 4, 50, 7, 5, 9):
