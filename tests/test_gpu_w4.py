@@ -130,19 +130,26 @@ def test_gemv_zero_input_and_code8():
 @pytest.mark.parametrize("shape", synth.layer_gemv_shapes(4096, 12288, 32, 8, 128),
                          ids=["qkv", "o", "gate_up", "down"])
 def test_gemv_full_9b_layer_sampled(shape):
-    """Full 9B-like layer matrices at m = 8 (the launch the bench times);
-    the oracle checks 96 sampled output rows of W."""
+    """Full 9B-like layer matrices at every verify row count m = 1..8 (the
+    launches the bench times); the oracle checks 96 sampled output rows of W
+    for each m, and the rows of a smaller m are those of the 8-row call."""
     n, k = shape
-    m = 8
-    announce(f"gemv full n={n} k={k}")
     w, s, packed = _weights(11, n, k)
-    x = synth.normal_bf16(synth.rng(12), (m, k))
-    y = sve.w4_gemv_m(dev_bf16(x), packed, n, k).cpu().numpy()
+    x = synth.normal_bf16(synth.rng(12), (8, k))
     cols = np.unique(np.concatenate([synth.rng(13).choice(n, 90, replace=False),
                                      [0, 15, 16, n - 17, n - 16, n - 1]]))
     want = ow4.gemv(x, w[cols], s[cols], k)
-    err = rel_l2_rows(y[:, cols], want)
-    assert err.max() <= GEMV_TOL, err
+    xd = dev_bf16(x)
+    y8 = None
+    for m in range(8, 0, -1):
+        announce(f"gemv full n={n} k={k} m={m}")
+        y = sve.w4_gemv_m(xd[:m].contiguous(), packed, n, k)
+        if y8 is None:
+            y8 = y
+        else:
+            assert torch.equal(y, y8[:m])  # row independence at full size
+        err = rel_l2_rows(y.cpu().numpy()[:, cols], want[:m])
+        assert err.max() <= GEMV_TOL, (m, err)
 
 
 # ---------------------------------------------------------------------------
@@ -203,6 +210,33 @@ def test_routed_bad_expert_gives_nan():
     announce("routed bad id")
     y = sve.w4_gemv_m_routed(x, ids, packed, e_all, n, k)
     assert torch.isfinite(y[0, 0]).all() and torch.isnan(y[0, 1]).all()
+
+
+def test_routed_moe_down_projection_sampled():
+    """35B-A3B-like expert layer, down projection: 256 experts of W2
+    [2048 x 512], each (row, expert slot) pair with its own input row
+    (x_per_slot), top-8 routing, m = 1 and 8; sampled output rows of every
+    pair against the oracle."""
+    e_all, n, k, topk = 256, 2048, 512, 8
+    g = synth.rng(31)
+    w_all = np.empty((e_all, n, k // 2), np.uint8)
+    s_all = np.empty((e_all, n, k // 32), np.uint16)
+    for e in range(e_all):
+        w_all[e], s_all[e] = synth.w4_weights(g, n, k)
+    packed = torch.cat([sve.w4_pack(dev_u8(w_all[e]), dev_f16(s_all[e]), n, k)
+                        for e in range(e_all)])
+    cols = np.unique(np.concatenate([synth.rng(32).choice(n, 40, replace=False), [0, n - 1]]))
+    for m in (1, 8):
+        announce(f"routed moe down full m={m}")
+        ids, _ = synth.routing_topk(synth.rng(33, m), m, e_all, topk)
+        h = synth.normal_bf16(synth.rng(34, m), (m, topk, k))
+        y = sve.w4_gemv_m_routed(dev_bf16(h), torch.from_numpy(ids).cuda(), packed, e_all, n, k,
+                                 x_per_slot=True).cpu().numpy()
+        for r in range(m):
+            for j in range(topk):
+                e = ids[r, j]
+                want = ow4.gemv(h[r, j][None], w_all[e][cols], s_all[e][cols], k)
+                assert rel_l2_rows(y[r, j][None, cols], want).max() <= GEMV_TOL, (m, r, j)
 
 
 def test_routed_moe_layer_sampled():
