@@ -10,7 +10,9 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsve.so")
+# SVE_LIBRARY selects another in-tree build of the same sources (the host
+# sanitizer build, libsve_hostsan.so, for the CPU tests of the C ABI)
+LIB_PATH = os.path.join(HERE, os.path.basename(os.environ.get("SVE_LIBRARY", "libsve.so")))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "sve.h")
 
 SVE_OK = 0

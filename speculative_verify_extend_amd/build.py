@@ -4,6 +4,11 @@
 
 Every source under csrc/ is compiled (in parallel) and linked into
 speculative_verify_extend_amd/libsve.so. Always rebuilds.
+
+It also links libsve_hostsan.so: the same kernels with the host side (the C
+ABI in api.cpp) built with AddressSanitizer and UndefinedBehaviorSanitizer,
+host code only (no sanitizer in GPU code). The CPU tests of the C ABI run
+against it in a child process that preloads the sanitizer runtime.
 """
 from __future__ import annotations
 
@@ -19,6 +24,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsve.so")
+LIB_HOSTSAN = os.path.join(HERE, "libsve_hostsan.so")
+# host-only sanitizers for the C ABI (each -fsanitize right after -Xarch_host)
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 ARCH = os.environ.get("SVE_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "kernels_w4.hip", "kernels_attn.hip", "kernels_slot.hip",
@@ -47,8 +56,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libsve)")
 
 
-def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, verbose: bool, extra=()) -> None:
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,21 +70,30 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print("\n".join(noisy), file=sys.stderr)
 
 
+def _link(objs, out: str, verbose: bool, extra=()) -> None:
+    out_tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", out_tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(out_tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="sve_build_") as tmp:
         objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
-        with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+        san_api = os.path.join(tmp, "api_hostsan.o")
+        with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES) + 1)) as ex:
             futs = [ex.submit(_compile, s, o, verbose) for s, o in zip(SOURCES, objs)]
+            futs.append(ex.submit(_compile, "api.cpp", san_api, verbose, HOSTSAN_FLAGS))
             for f in futs:
                 f.result()
-        out_tmp = LIB + ".tmp"
-        cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"linking libsve.so failed:\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        _link(objs, LIB, verbose)
+        _link([san_api] + [o for s, o in zip(SOURCES, objs) if s != "api.cpp"], LIB_HOSTSAN,
+              verbose, ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-shared-libsan"])
     return LIB
 
 
