@@ -364,6 +364,55 @@ int plan_mfma(sve_ctx* c, AttnParams& p) {
   return SVE_OK;
 }
 
+// Row-tile path for a call: when 32-row blocks leave the chip with fewer
+// than 192 workgroups (mid-size extends, such as a ~135-row turn of a 7B-like
+// layer: 16-row blocks, no key splits, no combine launch). Measured on the
+// agent replay (graph replays, 32 layers): 13-24% less per layer than the
+// split MFMA path at turns 2-7 (134-135 new rows over 727-1399 cached), even
+// at turns 8-9; the split path stays far ahead for long prefills (turn 1,
+// 727 rows) and is kept from 192 workgroups on.
+bool rows_fits(const AttnParams& p) {
+  long long blocks32 = 0;
+  for (int s = 0; s < p.nseg; ++s) blocks32 += (long long)p.Hkv * ((p.seg[s].m * p.g + 31) / 32);
+  return blocks32 < 192;
+}
+
+// Row-tile path: no key splits; a workgroup covers 16 * rt packed rows of
+// one KV head and every key they see. rt = 2 unless that leaves the chip
+// with fewer than 192 workgroups (then 16-row blocks).
+int plan_rows(sve_ctx* c, AttnParams& p) {
+  const bool fused = env_int("SVE_FUSED_APPEND", 1) != 0;
+  long long packed = 0;
+  for (int s = 0; s < p.nseg; ++s) packed += (long long)p.Hkv * ((p.seg[s].m * p.g + 31) / 32);
+  int rt = env_int("SVE_ROWS_RT", 0);
+  if (rt != 1 && rt != 2) rt = packed >= 192 ? 2 : 1;
+  p.rows_rt = rt;
+  int blocks = 0, rows = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    AttnSeg& sg = p.seg[s];
+    sg.row_blocks = (sg.m * p.g + 16 * rt - 1) / (16 * rt);
+    sg.head_blocks = sg.row_blocks;
+    sg.splits = 1;
+    sg.split_keys = sg.P + sg.m;
+    sg.tiled = 0;
+    sg.tail_split = 0;
+    sg.new_tile0 = fused ? 0 : -1;  // >= 0: keys at or past P come from the call's rows
+    sg.append_blocks = 0;
+    sg.append_begin = 0;
+    sg.block_begin = blocks;
+    sg.row_begin = rows;
+    blocks += p.Hkv * sg.row_blocks;
+    rows += sg.m;
+  }
+  p.total_blocks = blocks;
+  p.total_rows = rows;
+  p.append_total = 0;
+  if (log_on())
+    fprintf(stderr, "[sve] extend: path=rows pieces=%d blocks=%d rows/block=%d fused=%d\n", p.nseg,
+            blocks, 16 * rt, (int)fused);
+  return SVE_OK;
+}
+
 // Choose the path, row blocks and key splits of every piece of a call.
 //   decode: every piece has at most 64 packed rows (m*g) per KV head; a
 //           workgroup covers 32 packed rows and a key split of whole
@@ -385,12 +434,17 @@ int plan_attention(sve_ctx* c, AttnParams& p, int& path) {
     path = kPathValu;
   else if (want && !strcmp(want, "mfma"))
     path = kPathMfma;
+  else if (want && !strcmp(want, "rows"))
+    path = kPathRows;
   else if (want && !strcmp(want, "decode"))
     path = max_r <= 64 ? kPathDecode : kPathMfma;
   else if (mfma_min > 0)
     path = (max_m >= mfma_min) ? kPathMfma : kPathValu;
+  else if (max_r <= 64)
+    path = kPathDecode;
   else
-    path = max_r <= 64 ? kPathDecode : kPathMfma;
+    path = rows_fits(p) ? kPathRows : kPathMfma;
+  if (path == kPathRows) return plan_rows(c, p);
   const int rpb = attn_rows_per_block(path);
   int base = 0;
   for (int s = 0; s < p.nseg; ++s) {

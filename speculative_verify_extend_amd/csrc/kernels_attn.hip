@@ -1471,11 +1471,432 @@ __global__ __launch_bounds__(256) void kv_read_kernel(const uint16_t* K, const u
 }
 
 // ---------------------------------------------------------------------------
+// Row-tile path: extends whose pieces have too few packed rows for 128-row
+// blocks to fill the chip without key splits. Workgroup = (piece, KV head,
+// block of 16*RT packed rows) over every key its rows see: no key split, no
+// partials, no combine launch. Its 8 waves hold the same rows and take the
+// 32-key tiles in turn (wave w: tiles w, w+8, ...), each wave with its own
+// LDS part for the K rows (32 x D) and one for the Vt columns (D x 32), filled
+// by direct loads (from L2 after the first workgroup of the XCD touched the
+// tile): the next tile's K part is requested once this tile's scores are
+// computed, its Vt part once this tile's value products are done. No
+// barrier inside the key loop: the two waves of a SIMD drift freely, one's
+// matrix products overlapping the other's softmax.
+// Keys at or past P come from the call's rows: K rows by direct loads, V
+// rows through registers, transposed into the Vt part (zero past m). The
+// waves' (max, sum, output) states are merged through LDS in a fixed order,
+// and the first row blocks of each KV head append the call's rows.
+// ---------------------------------------------------------------------------
+constexpr int kRowsWaves = 8;
+
+// Vt part of a 32-key tile: row d holds four 16-byte chunks (8 keys each),
+// chunk c at position c ^ ((d >> 2) & 3), so that one value operand read
+// (16 consecutive rows, one chunk) meets 16 distinct bank groups.
+__device__ __forceinline__ int vswz4(int d, int c) { return c ^ ((d >> 2) & 3); }
+
+template <int D, int RT, bool ONE>
+__global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
+
+  constexpr int DC = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int CPR = D / 8;          // 16-byte chunks per K row
+  constexpr int ROWS = 16 * RT;
+  constexpr int PART = 32 * D;        // bf16 elements of a K (or Vt) part
+  constexpr int NK = PART * 2 / 1024; // 1 KB requests per part
+  constexpr int KPS = 64 / CPR;       // keys per K request
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kRowsWaves][2][PART];  // [wave][K|Vt]
+  __shared__ float wml[kRowsWaves][RT][2][64];                                // (max, sum)
+
+  const int L = xcd_linear(blockIdx.x, gridDim.x);
+  const SegRef ref = ONE ? SegRef{0, L} : find_seg(prm, L);
+  const AttnSeg& sg = prm.seg[ONE ? 0 : ref.s];
+  const int g = prm.g, Hq = prm.Hq, Hkv = prm.Hkv, cap = prm.cap;
+  const int P = sg.P, m = sg.m, R = m * g;
+  const int kvh = ref.local / sg.row_blocks;
+  const int rb = ref.local - kvh * sg.row_blocks;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, col = lane & 15;
+  const int row0 = rb * ROWS;
+  const int last = min(R - 1, row0 + ROWS - 1);
+  const int kend = P + last / g + 1;   // the block's rows see keys [0, kend)
+  const int min_lim = P + row0 / g;    // smallest last key of the block's rows
+  // Keys [0, pc) come from the store in 32-key tiles from key 0 (the last one
+  // cut at pc); keys [pc, kend) from the call's rows in 32-key tiles from pc.
+  // pc = P, or kend when the rows were appended beforehand.
+  const int pc = sg.new_tile0 >= 0 ? P : kend;
+  const int ncached = (pc + 31) >> 5;
+  const int ntiles = ncached + (kend > pc ? (kend - pc + 31) >> 5 : 0);
+  auto tile_key = [&](int t) { return t < ncached ? 32 * t : pc + 32 * (t - ncached); };
+
+  int lim[RT];
+  bf16x8 qreg[RT][DC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int pr = row0 + 16 * rt + col;
+    lim[rt] = pr < R ? P + pr / g : 0;  // padded rows read a live query row; never stored
+  }
+  f32x4 O[RT][DT];
+  float mref[RT], lrun[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    mref[rt] = -INFINITY;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint16_t* Kg = sg.K + (size_t)kvh * cap * D;
+  const uint16_t* Vg = sg.Vt + (size_t)kvh * D * cap;
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Kg), (short)0, cap * D * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Vg), (short)0, D * cap * 2, kBufWord3);
+  // the call's rows of this KV head (row r at r * Hkv * D); reads past row
+  // m-1 return zeros
+  const int new_bytes = ((m - 1) * Hkv + 1) * D * 2;
+  const __amdgpu_buffer_rsrc_t nkrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(sg.nk + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t nvrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(sg.nv + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
+  const float cs = prm.c;
+  uint16_t* Ks = lds[wave][0];
+  uint16_t* Vs = lds[wave][1];
+
+  // K part of tile t: request u fills chunk positions 64u + lane (key
+  // (64u + lane) / CPR of the tile, slot (64u + lane) % CPR) with the row's
+  // chunk kswz(key, slot): from the store for a cached tile (stale rows past
+  // pc are masked), from the call's rows for a new one (zeros past m). A
+  // tile index past the last one requests nothing that lands (every offset
+  // out of range), so that every tile issues the same NK requests.
+  // (The swizzle is computed into a variable before each request: called
+  // inside the builtin's argument list, the host compiler drops the kernel's
+  // launch stub.)
+  auto k_issue = [&](int t) {
+    const int kt = tile_key(t);
+    const bool live = t < ntiles;
+    if (t < ncached || !live) {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const int pos = 64 * u + lane, key = pos / CPR, slot = pos % CPR;
+        const int sw = kswz<D>(key, slot) * 8;  // (a variable: see the note above)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krsrc, (lds_void*)&Ks[512 * u], 16,
+            live ? (key * D + sw) * 2 : (int)0x80000000, live ? kt * D * 2 : 0,
+            0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) {
+        const int pos = 64 * u + lane, key = pos / CPR, slot = pos % CPR;
+        const int sw = kswz<D>(key, slot) * 8;  // (a variable: see the note above)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            nkrsrc, (lds_void*)&Ks[512 * u], 16,
+            ((kt + key - P) * Hkv * D + sw) * 2, 0, 0, 0);
+      }
+    }
+  };
+  // Vt part of tile t. Cached tile: the store's 8-key chunks by direct loads
+  // (request u: rows 16u .. 16u+15, lane -> row 16u + lane / 4, slot lane %
+  // 4); chunks from pc on read as zeros (out of range), and the keys from pc
+  // on inside the chunk holding pc are zeroed once it has landed. New tile:
+  // the call's V rows into registers (vreg, zeros past m), transposed into
+  // the part once they have landed. NK requests either way.
+  u32x4 vreg[NK];
+  const int vd = lane >> 2, vslot = lane & 3;
+  const int vloc = (vd * cap + vswz4(vd, vslot) * 8) * 2;
+  auto v_issue = [&](int t) {
+    const int kt = tile_key(t);
+    if (t < ncached || t >= ntiles) {
+      const bool live = t < ntiles;
+      const int k8 = kt + 8 * vswz4(vd, vslot);
+      const int voff = live && k8 < pc ? vloc : (int)0x80000000;
+#pragma unroll
+      for (int u = 0; u < NK; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)&Vs[512 * u], 16, voff,
+                                                 live ? kt * 2 + 32 * u * cap : 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int item = 64 * j + lane, key = item / CPR, c = item % CPR;
+        vreg[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       nvrsrc, ((kt + key - P) * Hkv * D + c * 8) * 2, 0, 0));
+      }
+    }
+  };
+  auto v_transpose = [&]() {
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int item = 64 * j + lane, key = item / CPR, c = item % CPR;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * c + e;
+        Vs[d * 32 + vswz4(d, key >> 3) * 8 + (key & 7)] =
+            (uint16_t)(vreg[j][e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  };
+  // the keys kt + key >= pc of the chunk holding pc (rows lane, lane + 64, ...)
+  auto v_zero_tail = [&](int kt) {
+    const int k0 = pc - kt;  // 1 .. 31: the tile's first key to clear
+    if ((k0 & 7) == 0) return;  // (the chunk starting at pc read as zeros)
+#pragma unroll
+    for (int d = lane; d < D; d += 64)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e >= (k0 & 7)) Vs[d * 32 + vswz4(d, k0 >> 3) * 8 + e] = 0;
+  };
+
+  f32x4 S[RT][2];
+  bf16x8 pb[RT];
+  auto qk = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) S[rt][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 2 * DC; ++q) {
+      const int dc = q >> 1, sub = q & 1;
+      const int kappa = 8 * (col >> 2) + 4 * sub + (col & 3);
+      const bf16x8 op = as_bf16x8(load16(Ks + kappa * D + kswz<D>(kappa, 4 * dc + kb) * 8));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) S[rt][sub] = mfma16x16x32(op, qreg[rt][dc], S[rt][sub]);
+    }
+  };
+  auto pv = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + col;
+      const bf16x8 op = as_bf16x8(load16(Vs + d * 32 + vswz4(d, kb) * 8));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) O[rt][dt] = mfma16x16x32(op, pb[rt], O[rt][dt]);
+    }
+  };
+  // online softmax of a tile: mask (only tiles reaching past the smallest
+  // limit), row maxima, a rescale when some row's max grew by more than 8
+  // (log2 units; only the rows that grew move), bf16 probabilities
+  auto softmax = [&](int kt, bool cached) {
+    // a row sees keys up to its limit; a cached tile's keys stop at pc
+    const int kcut = cached ? pc : 0x7FFFFFFF;
+    if (kt + 31 > min_lim || kt + 31 >= kcut) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt + 8 * kb + 4 * sub + i;
+            S[rt][sub][i] = ((key <= lim[rt]) & (key < kcut)) ? S[rt][sub][i] : -INFINITY;
+          }
+    }
+    float mcand[RT];
+    bool grow = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[rt][sub][i]);
+      mcand[rt] = max4_rows(mx) * cs;
+      grow |= mcand[rt] > mref[rt] + 8.f;
+    }
+    if (__ballot(grow) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bool up = mcand[rt] > mref[rt] + 8.f;
+        const float alpha = up ? fast_exp2(mref[rt] - mcand[rt]) : 1.f;
+        mref[rt] = up ? mcand[rt] : mref[rt];
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[rt][dt][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float muse = (mref[rt] == -INFINITY) ? 0.f : mref[rt];
+      float psum = lrun[rt];
+      u32x4 pk;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = fast_exp2(fmaf(S[rt][sub][i], cs, -muse));
+          const float p1 = fast_exp2(fmaf(S[rt][sub][i + 1], cs, -muse));
+          const uint32_t w = pack_bf16x2(p0, p1);
+          pk[2 * sub + (i >> 1)] = w;
+          psum = dot2_bf16(w, 0x3F803F80u, psum);  // + both bf16 values exactly
+        }
+      pb[rt] = as_bf16x8(pk);
+      lrun[rt] = psum;
+    }
+  };
+
+  const int nmine = ntiles > wave ? (ntiles - 1 - wave) / kRowsWaves + 1 : 0;
+  k_issue(wave);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int pr = row0 + 16 * rt + col;
+    const bool valid = pr < R;
+    const int i = valid ? pr / g : 0;
+    const int qh = kvh * g + (valid ? pr % g : 0);
+    const uint16_t* qrow = sg.q + ((size_t)i * Hq + qh) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qreg[rt][dc] = as_bf16x8(load16(qrow + 32 * dc + 8 * kb));
+  }
+  // the queries and the first K part in; from here on every tile issues NK
+  // K requests after its scores and NK Vt requests after its products
+  wait_vmem<0>();
+  v_issue(wave);
+  for (int j = 0; j < nmine; ++j) {
+    const int t = wave + kRowsWaves * j, kt = tile_key(t);
+    const bool cached = t < ncached;
+    wait_vmem<NK>();  // K(t) in; Vt(t) may be in flight
+    qk();
+    // (every K operand read has returned before the part is refilled)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_sched_barrier(0);
+    k_issue(t + kRowsWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(kt, cached);
+    wait_vmem<NK>();  // Vt(t) in; K(t+8) may be in flight
+    if (!cached)
+      v_transpose();
+    else if (kt + 31 >= pc)
+      v_zero_tail(kt);
+    pv();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_sched_barrier(0);
+    v_issue(t + kRowsWaves);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the requests for the tile past the last one: nothing lands, but they
+  // must have completed before LDS is reused
+  wait_vmem<0>();
+
+  // merge the 8 waves (same lane = same rows and columns): each hands over
+  // (max, row sum) and O; wave w then finishes column tiles w, w + 8, ...
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = lrun[rt];
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    lrun[rt] = l;
+  }
+  __syncthreads();  // every wave is done with its parts
+  f32x4* xo = reinterpret_cast<f32x4*>(&lds[0][0][0]);  // [wave][RT][DT][64 lanes]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    wml[wave][rt][0][lane] = mref[rt];
+    wml[wave][rt][1][lane] = lrun[rt];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) xo[((wave * RT + rt) * DT + dt) * 64 + lane] = O[rt][dt];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int pr = row0 + 16 * rt + col;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kRowsWaves; ++w) M = fmaxf(M, wml[w][rt][0][lane]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float sw[kRowsWaves], Lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowsWaves; ++w) {
+      sw[w] = fast_exp2(wml[w][rt][0][lane] - Mu);
+      Lt += wml[w][rt][1][lane] * sw[w];
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    if (pr >= R) continue;
+    const size_t orow = ((size_t)(pr / g) * Hq + kvh * g + pr % g) * D;
+    for (int dt = wave; dt < DT; dt += kRowsWaves) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kRowsWaves; ++w) {
+        const f32x4 ow = xo[((w * RT + rt) * DT + dt) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] += sw[w] * ow[i];
+      }
+      u32x2 w2;
+      w2[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+      w2[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+      *reinterpret_cast<u32x2*>(sg.out + orow + 16 * dt + 4 * kb) = w2;
+    }
+  }
+
+  // Append the call's rows [P, P+m) of this KV head (row blocks rb < A take
+  // the 64-key tiles T0 + rb, T0 + rb + A, ... of the range). K rows are
+  // copied; V rows go through LDS as [key][D + 2] (odd dword stride: the
+  // column reads below meet distinct banks) and leave as 16-byte pieces of 8
+  // keys of one column, key by key in the pieces holding P or P+m. No
+  // workgroup of the call reads these positions except inside the 8-key
+  // chunk holding P, whose values at or past P it replaces in LDS.
+  const int A = min(sg.row_blocks, kAppendBlocks);
+  if (sg.new_tile0 >= 0 && !sg.no_append && rb < A) {
+    constexpr int VST = D + 2;
+    uint16_t* Va = &lds[0][0][0];  // [64][VST]
+    uint16_t* Kw = const_cast<uint16_t*>(Kg);
+    uint16_t* Vw = const_cast<uint16_t*>(Vg);
+    const uint16_t* nkh = sg.nk + (size_t)kvh * D;
+    const uint16_t* nvh = sg.nv + (size_t)kvh * D;
+    const int wt = threadIdx.x;
+    const int T0 = P / 64, T1 = (P + m - 1) / 64;
+    __syncthreads();  // the merge's reads of LDS are done
+    for (int T = T0 + rb; T <= T1; T += A) {
+      for (int it = wt; it < 64 * CPR; it += 512) {
+        const int key = it / CPR, c = it % CPR, k = 64 * T + key;
+        if (k >= P && k < P + m) {
+          const size_t src = (size_t)(k - P) * Hkv * D + c * 8;
+          store16(Kw + (size_t)k * D + c * 8, load16(nkh + src));
+          const u32x4 v = load16(nvh + src);
+          uint32_t* row = reinterpret_cast<uint32_t*>(Va + key * VST + c * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) row[e] = v[e];
+        }
+      }
+      __syncthreads();
+      for (int it = wt; it < D * 8; it += 512) {
+        const int j8 = it & 7, d = it >> 3, k8 = 64 * T + 8 * j8;
+        if (k8 + 8 <= P || k8 >= P + m) continue;
+        uint16_t x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = Va[(8 * j8 + e) * VST + d];
+        uint16_t* dst = Vw + (size_t)d * cap + k8;
+        if (k8 >= P && k8 + 8 <= P + m) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (uint32_t)x[2 * e] | ((uint32_t)x[2 * e + 1] << 16);
+          store16(dst, w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k8 + e >= P && k8 + e < P + m) dst[e] = x[e];
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 
 int attn_rows_per_block(int path) {
   return path == kPathValu ? kValuRows : path == kPathDecode ? kDecRowsPerBlock : 64 * 2;
+}
+
+template <int D, bool ONE>
+static void launch_rows(const AttnParams& p, hipStream_t st) {
+  if (p.rows_rt == 1)
+    hipLaunchKernelGGL((attn_rows_kernel<D, 1, ONE>), dim3(p.total_blocks), dim3(64 * kRowsWaves),
+                       0, st, p);
+  else
+    hipLaunchKernelGGL((attn_rows_kernel<D, 2, ONE>), dim3(p.total_blocks), dim3(64 * kRowsWaves),
+                       0, st, p);
 }
 
 hipError_t launch_kv_append(const AttnParams& p, hipStream_t st) {
@@ -1538,6 +1959,12 @@ hipError_t launch_attn(const AttnParams& p, int path, hipStream_t st) {
       hipLaunchKernelGGL(attn_valu_kernel<128>, grid, block, 0, st, p);
     else
       hipLaunchKernelGGL(attn_valu_kernel<64>, grid, block, 0, st, p);
+  } else if (path == kPathRows) {
+    const bool one = p.nseg == 1;
+    if (p.D == 128)
+      one ? launch_rows<128, true>(p, st) : launch_rows<128, false>(p, st);
+    else
+      one ? launch_rows<64, true>(p, st) : launch_rows<64, false>(p, st);
   } else {
     const bool one = p.nseg == 1;
     if (p.D == 128)

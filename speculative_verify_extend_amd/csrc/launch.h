@@ -85,9 +85,10 @@ struct AttnParams {
   int append_total;    // combine-kernel append workgroups (before the combine's own)
   float c;             // log2(e) / sqrt(D)
   int dec_rt, dec_ns;  // decode path: 16-row tiles per block (1, 2), steps per round (1, 2)
+  int rows_rt;         // row-tile path: 16-row tiles per block (1, 2)
 };
 
-enum AttnPath { kPathValu = 0, kPathMfma = 1, kPathDecode = 2 };
+enum AttnPath { kPathValu = 0, kPathMfma = 1, kPathDecode = 2, kPathRows = 3 };
 
 // rows of packed (query row, head-in-group) per workgroup for each path
 int attn_rows_per_block(int path);

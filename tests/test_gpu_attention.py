@@ -17,8 +17,9 @@ pytestmark = pytest.mark.gpu
 ATTN_TOL = 1e-2  # max-abs against the fp64 oracle
 
 PATHS = {"valu": dict(SVE_MFMA_MIN_ROWS=100000), "mfma": dict(SVE_MFMA_MIN_ROWS=1),
-         "decode": dict(SVE_ATTN_PATH="decode")}  # decode: pieces of <= 64 packed rows
-ALL_PATHS = ["valu", "mfma", "decode"]
+         "decode": dict(SVE_ATTN_PATH="decode"),  # decode: pieces of <= 64 packed rows
+         "rows": dict(SVE_ATTN_PATH="rows")}      # row tiles over every key, no split
+ALL_PATHS = ["valu", "mfma", "decode", "rows"]
 
 
 @pytest.fixture(autouse=True)
@@ -38,11 +39,12 @@ def _run_case(hq, hkv, d, prefix, m, path, seed=0, split=0, prefill_path=None):
     toks = np.arange(prefix + m, dtype=np.int32)
     slot, reused = st.kv_slot_select(toks)
     assert (slot, reused) == (0, 0)
+    # (path None: the library's own choice)
     if prefix:
-        with env(**PATHS[prefill_path or path]):
+        with env(**PATHS.get(prefill_path or path, {})):
             st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]),
                            dev_bf16(c["v_prefix"]))
-    with env(SVE_KV_SPLIT=split, **PATHS[path]):
+    with env(SVE_KV_SPLIT=split, **PATHS.get(path, {})):
         out = st.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"]))
     k_all = np.concatenate([c["k_prefix"], c["k"]])
     v_all = np.concatenate([c["v_prefix"], c["v"]])
@@ -132,7 +134,15 @@ def test_turn9_full_size():
     """Agent-turn replay turn 9: 1668 cached + 254 new rows, 28 q / 4 KV heads,
     D 128, default launch configuration (the one the bench times)."""
     announce("turn9 full")
-    got, want, _, _ = _run_case(28, 4, 128, 1668, 254, "mfma", seed=2)
+    got, want, _, _ = _run_case(28, 4, 128, 1668, 254, None, seed=2)
+    assert np.abs(got - want).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("path", ["mfma", "rows"])
+def test_turn9_full_size_each_path(path):
+    """Turn 9 on each of the two many-row kernels, forced."""
+    announce(f"turn9 full path={path}")
+    got, want, _, _ = _run_case(28, 4, 128, 1668, 254, path, seed=2)
     assert np.abs(got - want).max() <= ATTN_TOL
 
 
@@ -140,16 +150,17 @@ def test_turn9_full_size():
                                   (8, 2, 128, 63, 300), (4, 1, 64, 130, 129),
                                   (8, 2, 128, 0, 200), (8, 2, 128, 700, 21)],
                          ids=lambda c: "h%d-%d-d%d-P%d-m%d" % c)
-def test_in_kernel_append_matches_separate_append(case):
-    """MFMA path: the attention kernel reads the new rows from the call's
-    inputs and appends them itself (the default), or a separate append
-    kernel writes them first. Both match the oracle, and the cached rows
-    they leave are the appended rows, bit for bit."""
+@pytest.mark.parametrize("path", ["mfma", "rows"])
+def test_in_kernel_append_matches_separate_append(case, path):
+    """MFMA and row-tile paths: the attention kernel reads the new rows from
+    the call's inputs and appends them itself (the default), or a separate
+    append kernel writes them first. Both match the oracle, and the cached
+    rows they leave are the appended rows, bit for bit."""
     hq, hkv, d, P, m = case
     for fused in (1, 0):
-        announce(f"in-kernel append={fused} {case}")
+        announce(f"in-kernel append={fused} {case} path={path}")
         with env(SVE_FUSED_APPEND=fused):
-            got, want, c, st = _run_case(hq, hkv, d, P, m, "mfma", seed=13)
+            got, want, c, st = _run_case(hq, hkv, d, P, m, path, seed=13)
         assert np.abs(got - want).max() <= ATTN_TOL
         kk, vv = st.kv_read(0, 0, 0, P + m)
         assert np.array_equal(host_bits(kk), np.concatenate([c["k_prefix"], c["k"]]))
@@ -267,18 +278,20 @@ def test_cached_rows_are_the_appended_rows(path):
     assert np.array_equal(host_bits(v), np.concatenate([c["v_prefix"], c["v"]]))
 
 
-def test_deterministic_repeats():
+@pytest.mark.parametrize("path", ["mfma", "rows"])
+def test_deterministic_repeats(path):
     hq, hkv, d, P, m = 28, 4, 128, 500, 60
     c = synth.attention_case(10, hq, hkv, d, P, m)
     st = _store(hq, hkv, d, P + m + 64, P + m)
     st.kv_slot_select(np.arange(P + m, dtype=np.int32))
     st.extend_attn(0, 0, dev_bf16(c["q_prefix"]), dev_bf16(c["k_prefix"]), dev_bf16(c["v_prefix"]))
     q, k, v = dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"])
-    announce("determinism")
-    first = st.extend_attn(0, 0, q, k, v)
-    for _ in range(100):
-        st.kv_truncate(0, P)
-        assert torch.equal(st.extend_attn(0, 0, q, k, v), first)
+    announce(f"determinism path={path}")
+    with env(**PATHS[path]):
+        first = st.extend_attn(0, 0, q, k, v)
+        for _ in range(100):
+            st.kv_truncate(0, P)
+            assert torch.equal(st.extend_attn(0, 0, q, k, v), first)
 
 
 def test_zero_rows_is_noop_and_state_errors():

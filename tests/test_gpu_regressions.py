@@ -53,6 +53,8 @@ STALE_PATHS = {
     "mfma-split3": dict(SVE_MFMA_MIN_ROWS=1, SVE_KV_SPLIT=3),
     "mfma-separate-append": dict(SVE_MFMA_MIN_ROWS=1, SVE_FUSED_APPEND=0),
     "valu": dict(SVE_MFMA_MIN_ROWS=100000),
+    "rows": dict(SVE_ATTN_PATH="rows"),
+    "rows-separate-append": dict(SVE_ATTN_PATH="rows", SVE_FUSED_APPEND=0),
 }
 
 
