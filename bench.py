@@ -340,6 +340,13 @@ def replay_turns(rp, passes=2, n_inputs=4):
     return res
 
 
+def replay_turns_alone(layers):
+    """replay_turns on a store of its own (for counter and trace runs)."""
+    rp = Replay(layers)
+    rp.select()
+    return replay_turns(rp)
+
+
 # ---------------------------------------------------------------------------
 # measured HBM ceilings
 # ---------------------------------------------------------------------------
@@ -396,9 +403,18 @@ def ceilings(backlog):
         sve.probe_compute(kind, blocks, iters, sink)
         ms = min(bracket([lambda k=kind: sve.probe_compute(k, blocks, iters, sink)] * 3, backlog))
         out[name] = round(per * waves * iters / (ms * 1e-3), 2)
+    # one CU filling LDS from L2: a 1 MB region read over and over, one
+    # 4-wave workgroup per CU, 128 tiles of 32 KB per wave
+    region = buf[:1 << 20]
+    sve.probe_read(region, 256, unroll=16, threads=256, mode=3)
+    ms = min(bracket([lambda: sve.probe_read(region, 256, unroll=16, threads=256, mode=3)] * 3,
+                     backlog))
+    out["l2_lds_fill_GBps_per_CU"] = round(4 * 128 * 32768 / (ms * 1e-3) / 1e9, 1)
     out["what"] = ("HBM: streaming read of 1 GiB (best of the read-probe launch shapes) and copy "
                    "of 512 MiB; compute: 2048 workgroups x 4 waves x 2000 iterations of 8 matrix "
-                   "products, 64 exponentials or 8 wave-wide 16-byte LDS reads; HIP events")
+                   "products, 64 exponentials or 8 wave-wide 16-byte LDS reads; L2 to LDS: a "
+                   "1 MB region read into LDS over and over by 256 workgroups of 4 waves (direct "
+                   "loads, 32 KB in flight per wave); HIP events")
     return out
 
 
@@ -830,7 +846,7 @@ def main():
                     help="time the headline from eager launches only (for counter runs)")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
     ap.add_argument("--only", choices=["gemv", "verify", "moe", "gemm", "accept", "ceilings",
-                                       "tiny", "content"],
+                                       "tiny", "content", "turns"],
                     help="run one section alone and print its JSON (counter and trace runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the copy probe (256 MiB, three times): the known byte count "
@@ -867,6 +883,7 @@ def main():
             "ceilings": lambda: ceilings(backlog),
             "tiny": lambda: tiny_config(backlog),
             "content": lambda: gemv_content(backlog),
+            "turns": lambda: replay_turns_alone(args.layers),
         }
         log(args.only)
         print(json.dumps({args.only: sections[args.only]()}, default=float), flush=True)

@@ -327,6 +327,12 @@ double sve_spec_break_even(double a, double b, int32_t k);
  *   mode 2: direct global-to-LDS loads, each wave a ring of `unroll` 1 KB
  *           slots (bytes % 1024 == 0, bytes < 2 GiB, threads/64 * unroll KB
  *           of LDS at most 160 KB): sink device uint32 [blocks].
+ *   mode 3: cache-resident direct-to-LDS fill: the region (bytes % 32768 ==
+ *           0, < 2 GiB; small enough to stay in L2, e.g. 1 MB) is read over
+ *           and over, every wave streaming 8 * `unroll` tiles of 32 KB
+ *           (32 one-KB requests each, at most 32 KB in flight per wave, 32 KB
+ *           of LDS per wave: at most 256 threads). Bytes moved = blocks *
+ *           threads/64 * 8 * unroll * 32768. sink device uint32 [blocks].
  * Plain copy: src to dst, `bytes` each (a multiple of 16), 256-thread blocks.
  * Errors: SVE_E_ARG, SVE_E_HIP. */
 int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t threads,

@@ -350,9 +350,12 @@ def spec_break_even(a: float, b: float, k: int) -> float:
 def probe_read(src: torch.Tensor, blocks: int, unroll: int = 4, threads: int = 256,
                mode: int = 0) -> torch.Tensor:
     """Streaming read of a device buffer (measurement probe). mode 0: plain
-    loads, 1: nontemporal loads, 2: direct global-to-LDS loads."""
+    loads, 1: nontemporal loads, 2: direct global-to-LDS loads, 3: the
+    buffer (small) read over and over into LDS, 8 * unroll tiles of 32 KB per
+    wave."""
     nbytes = src.numel() * src.element_size()
-    sink = torch.empty(blocks * (1 if mode == 2 else threads), dtype=torch.int32, device=src.device)
+    sink = torch.empty(blocks * (1 if mode >= 2 else threads), dtype=torch.int32,
+                       device=src.device)
     check(_lib.load().sve_probe_read(_ptr(src), nbytes, blocks, threads, unroll, mode, _ptr(sink),
                                      _stream()))
     return sink

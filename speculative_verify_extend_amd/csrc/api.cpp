@@ -1086,7 +1086,10 @@ int sve_probe_read(const void* src, size_t bytes, int32_t blocks, int32_t thread
     return fail(nullptr, SVE_E_ARG, "threads must be a multiple of 64 in 64..1024");
   if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
     return fail(nullptr, SVE_E_ARG, "unroll must be 1, 2, 4, 8 or 16");
-  if (mode < 0 || mode > 2) return fail(nullptr, SVE_E_ARG, "mode must be 0, 1 or 2");
+  if (mode < 0 || mode > 3) return fail(nullptr, SVE_E_ARG, "mode must be 0..3");
+  if (mode == 3 && (bytes % 32768 || bytes > 0x7FFFFFFFu || threads > 256))
+    return fail(nullptr, SVE_E_ARG,
+                "cache-resident LDS mode: bytes % 32768 == 0, < 2 GiB, at most 256 threads");
   if (mode == 2 && (bytes % 1024 || bytes > 0x7FFFFFFFu ||
                     (size_t)(threads / 64) * unroll * 1024 > 160 * 1024))
     return fail(nullptr, SVE_E_ARG, "LDS mode: bytes % 1024 == 0, < 2 GiB, ring within 160 KB");

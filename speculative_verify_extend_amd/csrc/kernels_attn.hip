@@ -1596,6 +1596,9 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
       }
     }
   };
+  // (The call's V rows are taken key-major: item (key, c) = (item % 32,
+  // item / 32), so that the transposed 2-byte writes of a column come from
+  // adjacent lanes and meet adjacent bytes.)
   // Vt part of tile t. Cached tile: the store's 8-key chunks by direct loads
   // (request u: rows 16u .. 16u+15, lane -> row 16u + lane / 4, slot lane %
   // 4); chunks from pc on read as zeros (out of range), and the keys from pc
@@ -1618,7 +1621,7 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
     } else {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
-        const int item = 64 * j + lane, key = item / CPR, c = item % CPR;
+        const int item = 64 * j + lane, key = item & 31, c = item >> 5;
         vreg[j] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                        nvrsrc, ((kt + key - P) * Hkv * D + c * 8) * 2, 0, 0));
@@ -1628,7 +1631,7 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   auto v_transpose = [&]() {
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      const int item = 64 * j + lane, key = item / CPR, c = item % CPR;
+      const int item = 64 * j + lane, key = item & 31, c = item >> 5;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = 8 * c + e;

@@ -7,6 +7,8 @@
 //     which hold no registers while in flight); grid, workgroup size and
 //     loads in flight per wave are the caller's, so a sweep finds the best
 //     launch shape for a given byte count;
+//   a cache-resident direct-to-LDS fill (a small region read over and over:
+//     the rate one CU fills LDS from L2);
 //   plain copy (counter calibration: a known number of bytes each way);
 //   compute: v_mfma_f32_16x16x32_bf16, v_mfma_f32_32x32x16_bf16 and
 //     v_mfma_f32_16x16x32_f16 issue rates, v_exp_f32 throughput, and LDS
@@ -73,6 +75,42 @@ __global__ __launch_bounds__(1024) void probe_read_lds_kernel(const uint8_t* __r
   wait_vmem<0>();
   __syncthreads();
   if (threadIdx.x == 0) sink[blockIdx.x] = (uint32_t)n + mine[lane];
+}
+
+// Cache-resident direct-to-LDS fill: every wave streams 32 KB tiles of a
+// small region (tile (block * W + wave) + t, cycling over the region), each
+// tile as 32 one-KB requests into two 16 KB halves of its own LDS, waiting
+// for a half's previous requests before refilling it (at most 32 KB in
+// flight per wave). With a region that fits in L2 this is the rate at which
+// one CU can fill LDS from L2 (the bound of a workgroup that reads every
+// tile once for few rows). The data is not consumed.
+__global__ __launch_bounds__(256) void probe_l2_lds_kernel(const uint8_t* __restrict__ src,
+                                                           size_t bytes, int tiles,
+                                                           uint32_t* __restrict__ sink) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];  // [W][2][16 KB]
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(src), (short)0, (int)bytes, kBufWord3);
+  const int ntile = (int)(bytes >> 15);
+  int tt = (int)(((size_t)blockIdx.x * W + wave) % ntile);
+  uint8_t* mine = ring + (size_t)wave * 32768;
+  for (int t = 0; t < tiles; ++t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (t > 0) wait_vmem<16>();  // this half's previous requests have landed
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(mine + h * 16384 + u * 1024), 16,
+                                                 lane * 16, tt * 32768 + h * 16384 + u * 1024, 0,
+                                                 0);
+    }
+    tt = tt + 1 == ntile ? 0 : tt + 1;
+  }
+  wait_vmem<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = (uint32_t)tiles + mine[lane];
 }
 
 __global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict__ src,
@@ -167,6 +205,15 @@ hipError_t launch_probe_read(const void* src, size_t bytes, int blocks, int thre
                              int mode, void* sink, hipStream_t st) {
   const dim3 g(blocks), b(threads);
   uint32_t* sk = (uint32_t*)sink;
+  if (mode == 3) {
+    const size_t lds = (size_t)(threads / 64) * 32768;
+    hipError_t e = hipFuncSetAttribute((const void*)probe_l2_lds_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(probe_l2_lds_kernel, g, b, lds, st, (const uint8_t*)src, bytes, 8 * unroll,
+                       sk);
+    return hipGetLastError();
+  }
   if (mode == 2) {
     const size_t lds = (size_t)(threads / 64) * unroll * 1024;
     auto go = [&](auto kern) {

@@ -115,7 +115,9 @@ def test_probe_arguments_fail_before_gpu_work(lib):
     assert read(threads=100) == _lib.SVE_E_ARG
     assert read(threads=2048) == _lib.SVE_E_ARG
     assert read(unroll=3) == _lib.SVE_E_ARG
-    assert read(mode=3) == _lib.SVE_E_ARG
+    assert read(mode=4) == _lib.SVE_E_ARG
+    assert read(mode=3, bytes=(1 << 20) + 1024) == _lib.SVE_E_ARG     # not whole 32 KB tiles
+    assert read(mode=3, threads=512) == _lib.SVE_E_ARG                # 32 KB of LDS per wave
     assert read(mode=2, bytes=(1 << 20) + 16) == _lib.SVE_E_ARG       # not whole 1 KB chunks
     assert read(mode=2, threads=1024, unroll=16) == _lib.SVE_E_ARG    # 256 KB ring > 160 KB of LDS
     assert lib.sve_probe_compute(5, 1, 1, p, None) == _lib.SVE_E_ARG
