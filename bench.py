@@ -297,14 +297,16 @@ class Replay:
         self.graph.replay()
 
 
-def replay_turns(rp, passes=2, n_inputs=4):
+def replay_turns(rp, passes=2, n_inputs=4, graph=True):
     """Every turn of the agent replay on the replay's store and rotated
     layers: turn t cuts the slot back to L_(t-1) resident rows (metadata
     only) and extends its m = L_t - L_(t-1) new rows in every layer. The
     slot's committed prompt is turn 9's, which starts with every earlier
     prompt, so no select is needed between turns. Per call: the kernel
-    durations the library records with HIP events (eager calls). The new
-    rows rotate over a few input buffers; the KV read per layer is the
+    durations the library records with HIP events (eager calls); with
+    `graph`, also the turn's calls captured in a HIP graph and replayed, on
+    the library's own choice of kernel and on each many-row path forced. The
+    new rows rotate over a few input buffers; the KV read per layer is the
     store's, distinct per layer."""
     wl = synth.WORKLOADS["replay7b"]
     lengths = list(wl["prompt_lengths"])[:9]  # turn 10's length is an extrapolation
@@ -337,14 +339,58 @@ def replay_turns(rp, passes=2, n_inputs=4):
         res[t] = {"cached": P, "new": m, "attn_us": r2(attn), "call_kernels_us": r2(call),
                   "tok_per_s": round(m / (call * 1e-6), 1), "attn_TFLOPs": round(tf, 1),
                   "attn_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if graph:
+            # the same pass captured in a HIP graph and replayed, on the
+            # library's own choice of kernel and on each many-row path forced
+            for name, path in (("graph_us_per_layer", None), ("graph_us_split_path", "mfma"),
+                               ("graph_us_row_tile_path", "rows")):
+                res[t][name] = r2(turn_graph_us(rp, P, m, ins, out, path))
+            one_pass()  # (the turn's rows resident again for the next turn's cut)
+            torch.cuda.synchronize()
     return res
 
 
+def turn_graph_us(rp, P, m, ins, out, path, reps=5):
+    """Per-layer time of one replay turn's extend calls (every layer) captured
+    in a HIP graph, best of `reps` replays; `path` forces SVE_ATTN_PATH."""
+    old = os.environ.get("SVE_ATTN_PATH")
+    if path:
+        os.environ["SVE_ATTN_PATH"] = path
+    else:
+        os.environ.pop("SVE_ATTN_PATH", None)
+    try:
+        n_in = len(ins)
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        rp.st.kv_truncate(0, P)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for layer in range(rp.layers):
+                q, k, v = ins[layer % n_in]
+                rp.st.extend_attn(0, layer, q[:m], k[:m], v[:m], out[:m])
+        torch.cuda.synchronize()
+        best = math.inf
+        for _ in range(reps):
+            rp.st.kv_truncate(0, P)
+            with Timer() as tm:
+                g.replay()
+            best = min(best, tm.ms / rp.layers * 1e3)
+        del g
+        rp.st.kv_truncate(0, P)
+        return best
+    finally:
+        if old is None:
+            os.environ.pop("SVE_ATTN_PATH", None)
+        else:
+            os.environ["SVE_ATTN_PATH"] = old
+
+
 def replay_turns_alone(layers):
-    """replay_turns on a store of its own (for counter and trace runs)."""
+    """replay_turns on a store of its own, eager calls only (for counter and
+    trace runs)."""
     rp = Replay(layers)
     rp.select()
-    return replay_turns(rp)
+    return replay_turns(rp, graph=False)
 
 
 # ---------------------------------------------------------------------------
