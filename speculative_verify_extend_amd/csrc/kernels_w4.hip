@@ -1069,6 +1069,175 @@ __global__ __launch_bounds__(256, 2) void w4_gemm_kernel(const uint16_t* __restr
     }
 }
 
+// Wide form: workgroup = four waves over 64 rows and 256 columns; wave w
+// owns columns 64w .. 64w+63 of the workgroup (4 x 4 tiles of 16 x 16, as
+// above). The activation operands of a quad (4 row tiles x 4 groups, 16 KB
+// of the packed x) reach a ring of three LDS slots by direct loads, two
+// quads ahead, each wave loading one row tile; all four waves read them.
+// Each wave loads its own weight tiles (nibbles and scales) straight into
+// registers two quads ahead and dequantises them there, so no weight goes
+// through LDS. Per 256 products a workgroup then fetches 34 KB (16 KB of
+// activations + 4 x 4.5 KB of weights) where the form above fetches 68.5 KB
+// (every wave its own 16 KB of activations), and the load return path is
+// what that form saturates. The price is four times the dequantisation
+// work (each wave dequantises the 64 columns it multiplies). 48 KB of LDS
+// and at most 168 registers keep three workgroups on a CU, so 592
+// workgroups (a 37888-column matrix at 254 rows) are resident at once.
+// Slots are separate LDS variables and the quad loop is unrolled by six
+// (three slots, two weight buffers), so every read names its slot and
+// buffer (the compiler then waits only for their loads).
+constexpr int kWideCols = 256;
+constexpr int kWideRows = 64;
+
+struct WideB {
+  u32x4 w[4];  // nibble dwords of the wave's 4 column tiles
+  u32x2 s[4];  // scale row (4 group scales) of each tile, lane r = row r
+};
+
+__global__ __launch_bounds__(256, 3) void w4_gemm_wide_kernel(
+    const uint16_t* __restrict__ xh, int m, int rows_pad, const uint8_t* __restrict__ nib,
+    const uint8_t* __restrict__ scl, int N, int K, int Q, int qps, int ncb, int nrb,
+    float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t as0[4][4][1024], as1[4][4][1024],
+      as2[4][4][1024];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = lane >> 4, r = lane & 15;
+  // workgroups are dealt to the eight XCDs in turn (b % 8); the row blocks
+  // of a column block take consecutive turns on one XCD, so its weights are
+  // fetched into that XCD's L2 once and hit there for the other row blocks
+  const int b = blockIdx.x, xcd = b & 7, turn = b >> 3;
+  const int rb = turn % nrb, cb = (turn / nrb) * 8 + xcd;
+  if (cb >= ncb) return;  // (whole workgroup, before any barrier)
+  const int m0 = rb * kWideRows;
+  const int n_tiles = (N + 15) / 16, G = K >> 5;
+  const int q0 = blockIdx.z * qps, q1 = min(Q, q0 + qps);
+  const int tile0 = cb * (kWideCols / 16) + wave * 4;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xh), (short)0, rows_pad * K * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(nib), (short)0, n_tiles * Q * 1024, kBufWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(scl), (short)0, n_tiles * Q * 128, kBufWord3);
+  // Requests for quads past the split (the loop runs a multiple of six)
+  // take a lane offset past every buffer's end: they return zeros without
+  // a fetch and keep the request counts uniform.
+  constexpr uint32_t kPast = 0x80000000u;
+
+  // this wave's row tile of quad q (groups 4q .. 4q+3, each clamped to a
+  // real group: groups past K meet weights of scale 0) into a slot: four
+  // requests
+  const int xrt = m0 / 16 + wave;
+  auto issue_a = [&](uint8_t (*sl)[4][1024], int q) {
+    const uint32_t vo = q < q1 ? lane * 16u : kPast + lane * 16u;
+    q = min(q, q1 - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = min(4 * q + j, G - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)&sl[wave][j][0], 16, vo,
+                                               (xrt * G + g) * 1024, 0, 0);
+    }
+  };
+  // the wave's four weight tiles of quad q: eight requests (tiles past N
+  // re-read the last tile; their columns are never stored)
+  auto issue_b = [&](WideB& wb, int q) {
+    const uint32_t vn = q < q1 ? lane * 16u : kPast + lane * 16u;
+    const uint32_t vs = q < q1 ? r * 8u : kPast + r * 8u;
+    q = min(q, q1 - 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tt = min(tile0 + t, n_tiles - 1);
+      wb.w[t] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(nrs, vn, (tt * Q + q) * 1024, 0));
+      wb.s[t] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, vs, (tt * Q + q) * 128, 0));
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[a][t] = zero4;
+
+  // products of one quad: activation slot sl, weights wb
+  auto quad = [&](uint8_t (*sl)[4][1024], const WideB& wb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 xa[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        xa[a] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&sl[a][j][lane * 16]));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t sw = wb.s[t][j >> 1] >> (16 * (j & 1));
+        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
+        const f16x2 s2 = {sc, sc};
+        bf[t] = __builtin_bit_cast(f16x8, w4_f16frag(wb.w[t][j], s2));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[a][t] = mfma16x16x32_f16(xa[a], bf[t], acc[a][t]);
+    }
+  };
+
+  // Issue order, as in the loop (quad i requests A(i+2) at its start and
+  // B(i+2) at its end): A(q0) B(q0) | A(q0+1) B(q0+1). At the start of
+  // quad q the requests after B(q) are A(q+1) and B(q+1): 4 + 8.
+  WideB B0, B1;
+  issue_a(as0, q0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_b(B0, q0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a(as1, q0 + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_b(B1, q0 + 1);
+  // Quads past the split keep their (empty) requests and barriers but skip
+  // the products. (With an early exit from the unrolled body, the loop head
+  // was reachable with a different request history, and the compiler then
+  // waited for every request before the first quad of each round.)
+  for (int qb = q0; qb < q1; qb += 6) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int q = qb + u;
+      // A(q) of every wave is in and every wave is done with quad q-1's
+      // slot, which A(q+2) now refills. A bare s_barrier after the
+      // count-based wait: a fenced one would also wait for the LDS writes
+      // of the quad still in flight.
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmem<12>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t(*cur)[4][1024] = u % 3 == 0 ? as0 : u % 3 == 1 ? as1 : as2;
+      uint8_t(*nxt)[4][1024] = u % 3 == 0 ? as2 : u % 3 == 1 ? as0 : as1;
+      issue_a(nxt, q + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      WideB& wb = (u & 1) ? B1 : B0;
+      if (q < q1) quad(cur, wb);  // uniform
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(wb, q + 2);
+    }
+  }
+  wait_vmem<0>();  // no request may land in LDS after the workgroup ends
+
+  // lane holds rows m0 + 16a + 4kb + i of column 16 (tile0 + t) + r
+  float* o = out + (size_t)blockIdx.z * m * N;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int col = 16 * (tile0 + t) + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * a + 4 * kb + i;
+        if (row < m && col < N) o[(size_t)row * N + col] = acc[a][t][i];
+      }
+    }
+}
+
 // y = sum of the splits' partial results, in split order
 __global__ __launch_bounds__(256) void w4_gemm_reduce_kernel(const float* __restrict__ ws, int ks,
                                                              long long mn, float* __restrict__ y) {
@@ -1081,13 +1250,42 @@ __global__ __launch_bounds__(256) void w4_gemm_reduce_kernel(const float* __rest
 
 // k splits of the GEMM: enough workgroups for two per compute unit, at most
 // kGemmMaxSplits and at most one per quad of 128 k
-int w4_gemm_splits(int m, int N, int K) {
+// Form of the GEMM: 0 = 256 rows x 64 columns per workgroup, 1 = wide (64
+// rows x 256 columns). The wide form is chosen when padding the rows to 256
+// would leave at least one wave of a workgroup without rows (m mod 256 in
+// 1..192): at 134 rows of a 7B-like layer it took 172.8 us against 191.9
+// (gate|up 67.4 against 84.7), at 254 rows 225.3 against 214.5, where the
+// wide form's four-fold dequantisation (vector work about equal to the
+// products' time) outweighs its halved operand traffic. SVE_GEMM_FORM=0|1
+// overrides.
+static int gemm_form(int m) {
+  const char* v = getenv("SVE_GEMM_FORM");
+  if (v && *v) return atoi(v) != 0;
+  const int rows_narrow = (m + kGemmGroupRows - 1) / kGemmGroupRows * kGemmGroupRows;
+  const int rows_wide = (m + kWideRows - 1) / kWideRows * kWideRows;
+  return rows_narrow - rows_wide >= kGemmWaveRows;
+}
+
+// quads per k split: enough workgroups for two per compute unit, at most
+// kGemmMaxSplits splits and at least one quad each; the wide form's quad
+// loop runs in rounds of six, so its count is rounded up to a multiple of
+// six (fewer, fuller splits instead of empty rounds)
+static int gemm_qps(int m, int N, int K) {
   const int Q = (K + 127) / 128;
-  const int base = ((N + kGemmCols - 1) / kGemmCols) * ((m + kGemmGroupRows - 1) / kGemmGroupRows);
+  const bool wide = gemm_form(m);
+  const int base =
+      wide ? ((N + kWideCols - 1) / kWideCols) * ((m + kWideRows - 1) / kWideRows)
+           : ((N + kGemmCols - 1) / kGemmCols) * ((m + kGemmGroupRows - 1) / kGemmGroupRows);
   int ks = std::max(1, std::min({512 / std::max(base, 1), kGemmMaxSplits, Q}));
   const int forced = getenv("SVE_GEMM_SPLITS") ? atoi(getenv("SVE_GEMM_SPLITS")) : 0;
   if (forced > 0) ks = std::min({forced, kGemmMaxSplits, Q});
-  const int qps = (Q + ks - 1) / ks;
+  int qps = (Q + ks - 1) / ks;
+  if (wide && forced <= 0 && ks > 1) qps = std::min(Q, (qps + 5) / 6 * 6);
+  return qps;
+}
+
+int w4_gemm_splits(int m, int N, int K) {
+  const int Q = (K + 127) / 128, qps = gemm_qps(m, N, K);
   return (Q + qps - 1) / qps;
 }
 
@@ -1107,10 +1305,10 @@ hipError_t launch_w4_gemm(const void* x, int m, const void* packed, int N, int K
   const int n_tiles = (N + 15) / 16, Q = (K + 127) / 128;
   const uint8_t* nib = (const uint8_t*)packed;
   const uint8_t* scl = nib + (size_t)n_tiles * Q * 1024;
-  const int ks = w4_gemm_splits(m, N, K);
-  const int qps = (Q + ks - 1) / ks;
+  const int qps = gemm_qps(m, N, K);
+  const int ks = (Q + qps - 1) / qps;
   // the kernel's buffer offsets are 32-bit
-  if ((size_t)n_tiles * Q * 1024 >= (1u << 31) || (size_t)m * K * 2 >= (1u << 31))
+  if ((size_t)n_tiles * Q * 1024 >= (1u << 31) || gemm_xh_bytes(m, K) >= (1u << 31))
     return hipErrorInvalidValue;
   const dim3 grid((N + kGemmCols - 1) / kGemmCols, (m + kGemmGroupRows - 1) / kGemmGroupRows, ks);
   uint16_t* xh = (uint16_t*)ws;
@@ -1119,7 +1317,15 @@ hipError_t launch_w4_gemm(const void* x, int m, const void* packed, int N, int K
   hipLaunchKernelGGL(w4_x_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
                      (const uint16_t*)x, m, K, pieces, xh);
   float* out = ks > 1 ? part : y;
-  hipLaunchKernelGGL(w4_gemm_kernel, grid, dim3(256), 0, st, xh, m, nib, scl, N, K, Q, qps, out);
+  if (gemm_form(m)) {
+    const int ncb = (N + kWideCols - 1) / kWideCols, nrb = (m + kWideRows - 1) / kWideRows;
+    const int rows_pad = (int)(gemm_xh_bytes(m, K) / ((size_t)K * 2));
+    const dim3 wgrid((unsigned)((ncb + 7) / 8 * 8 * nrb), 1, ks);
+    hipLaunchKernelGGL(w4_gemm_wide_kernel, wgrid, dim3(256), 0, st, xh, m, rows_pad, nib, scl, N,
+                       K, Q, qps, ncb, nrb, out);
+  } else {
+    hipLaunchKernelGGL(w4_gemm_kernel, grid, dim3(256), 0, st, xh, m, nib, scl, N, K, Q, qps, out);
+  }
   if (ks > 1) {
     const long long mn = (long long)m * N;
     hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
@@ -1183,8 +1389,12 @@ hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K
     // than contiguous runs on a 24576x4096 matrix); SVE_GEMV_STRIDE=0 keeps
     // the contiguous runs
     const int strided = env_int_w4("SVE_GEMV_STRIDE", 1);
+    // C0 terms once per wave: with one quad per wave, and for single tiles
+    // (4096x4096 at m = 1 / 8: 5.28 / 5.96 us against 5.60 / 6.48 recomputed);
+    // runs of two-quad waves recompute them (6144x4096 and 24576x4096 were
+    // 0.1-0.7 us slower hoisted)
     const int hoist_env = env_int_w4("SVE_GEMV_HOIST", -1);
-    const bool hoist = hoist_env >= 0 ? hoist_env != 0 : qpw == 1;
+    const bool hoist = hoist_env >= 0 ? hoist_env != 0 : (qpw == 1 || single);
 #define SVE_SHORT(Q_, S_, H_, D_)                                                              \
   hipLaunchKernelGGL((w4_gemv_short_kernel<Q_, S_, H_, D_>), dim3(grid), dim3(64 * W), 0, st, \
                      xp, m, nib, scl, N, K, Q, n_tiles, strided, y)

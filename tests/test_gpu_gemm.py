@@ -147,3 +147,23 @@ def test_gemm_full_7b_layer_sampled(shape):
                                      [0, 15, 16, 63, 64, n - 65, n - 17, n - 1]]))
     err = rel_l2_rows(y[:, cols], ow4.gemv(x, w[cols], s[cols], k))
     assert err.max() <= GEMM_TOL, err
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("m,n,k", [(16, 100, 96), (70, 1000, 2048), (254, 520, 3584),
+                                   (300, 4608, 640)])
+def test_gemm_forms_agree_bitwise(m, n, k, splits):
+    """The two workgroup forms (256 rows x 64 columns; 64 rows x 256
+    columns) multiply the same fp16 operands in the same order, so under the
+    same k splits their outputs are bitwise equal; both match the oracle
+    (ragged rows and columns, quads past a split, several row blocks)."""
+    announce(f"gemm forms m={m} n={n} k={k} splits={splits}")
+    w, s, packed = _weights(35, n, k)
+    x = synth.normal_bf16(synth.rng(36, m, n, k), (m, k))
+    out = {}
+    for form in (0, 1):
+        with env(SVE_GEMM_FORM=form, SVE_GEMM_SPLITS=splits):
+            out[form] = sve.w4_gemm(dev_bf16(x), packed, n, k)
+    assert torch.equal(out[0], out[1])
+    err = rel_l2_rows(out[1].cpu().numpy(), ow4.gemv(x, w, s, k))
+    assert err.max() <= GEMM_TOL, err
