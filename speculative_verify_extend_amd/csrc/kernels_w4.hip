@@ -698,12 +698,6 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
   __shared__ int s_next;
   const int ps = blockIdx.y;
   const int npairs = m * topk;
-  for (int t = threadIdx.x; t < npairs; t += blockDim.x) sid[t] = ids[t];
-  __syncthreads();
-  const int e = sid[ps];
-  bool earlier = false;
-  for (int t = threadIdx.x; t < ps; t += blockDim.x) earlier |= sid[t] == e;
-  if (__syncthreads_or(earlier)) return;  // an earlier pair slot owns this expert
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -711,6 +705,21 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
   const int G = K >> 5;
   const int t0 = blockIdx.x * run, t1 = min(n_tiles, t0 + run);
   if (t0 >= t1) return;
+  // Every wave reads the routing table into registers (pair lane + 64c)
+  // and decides by itself, with no barrier, whether an earlier pair slot
+  // names the same expert (then that slot owns it); every wave reaches the
+  // same answer. The owner's first weight requests go out right after, so
+  // the weight stream does not wait for the pair gathering below.
+  const int e = ids[ps];
+  int tid[kRoutedMaxPairs / 64];
+  bool earlier = false;
+#pragma unroll
+  for (int c = 0; c < kRoutedMaxPairs / 64; ++c) {
+    const int p = lane + 64 * c;
+    tid[c] = p < npairs ? ids[p] : -1;
+    earlier |= p < ps && tid[c] == e;
+  }
+  if (__ballot(earlier) != 0ull) return;  // (uniform)
   const int nt = t1 - t0;
   const bool valid = (e >= 0 && e < E);
   const uint8_t* nib = packed_all + (valid ? (size_t)e * expert_bytes : 0);
@@ -720,6 +729,26 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
   const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t loff = lane * 16, soff = r * 8;
+  auto issue = [&](int t, TileBuf<QPW>& b) {
+    t = min(t, t1 - 1);
+#pragma unroll
+    for (int a = 0; a < QPW; ++a) {
+      const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
+      b.w[a] = load16(nib + blk * 1024 + loff);
+      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+    }
+  };
+  // the first pass's first two tiles (an invalid expert id reads expert 0's,
+  // unused: its outputs are NaN)
+  TileBuf<QPW> A, B;
+  issue(t0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(t0 + 1, B);
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave == 0)
+#pragma unroll
+    for (int c = 0; c < kRoutedMaxPairs / 64; ++c)
+      if (lane + 64 * c < npairs) sid[lane + 64 * c] = tid[c];
 
   int start = ps;  // pairs with this expert all sit at or after ps
   while (true) {
@@ -770,15 +799,6 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
                                   u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                              xrs, xoff + 64u * min(4 * (q0 + a) + j, G - 1), 0, 0)))
                             : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-      auto issue = [&](int t, TileBuf<QPW>& b) {
-        t = min(t, t1 - 1);
-#pragma unroll
-        for (int a = 0; a < QPW; ++a) {
-          const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
-          b.w[a] = load16(nib + blk * 1024 + loff);
-          b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
-        }
-      };
       auto consume = [&](const TileBuf<QPW>& b) {
         f32x4 acc = zero4;
 #pragma unroll
@@ -805,12 +825,8 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
         }
         __syncthreads();
       };
-      // double-buffered walk over the run (as in the dense short kernel)
-      TileBuf<QPW> A, B;
-      issue(t0, A);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(t0 + 1, B);
-      __builtin_amdgcn_sched_barrier(0);
+      // double-buffered walk over the run (as in the dense short kernel);
+      // tiles t0 and t0+1 are already requested
       int tb = t0;
       for (int t = t0; t < t1; t += 2) {
         const f32x4 acc0 = consume(A);
@@ -833,6 +849,11 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
     }
     if (next >= npairs) break;
     start = next;
+    // the next pass walks the run again from its first tiles
+    issue(t0, A);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t0 + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
