@@ -1504,7 +1504,11 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   constexpr int PART = 32 * D;        // bf16 elements of a K (or Vt) part
   constexpr int NK = PART * 2 / 1024; // 1 KB requests per part
   constexpr int KPS = 64 / CPR;       // keys per K request
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kRowsWaves][2][PART];  // [wave][K|Vt]
+  // K parts and Vt parts are separate arrays, so the compiler can tell a
+  // read of one from a pending direct load into the other (with one array
+  // indexed by the wave it waited for every request before the scores)
+  __shared__ __attribute__((aligned(16))) uint16_t kpart[kRowsWaves][PART];
+  __shared__ __attribute__((aligned(16))) uint16_t vpart[kRowsWaves][PART];
   __shared__ float wml[kRowsWaves][RT][2][64];                                // (max, sum)
 
   const int L = xcd_linear(blockIdx.x, gridDim.x);
@@ -1560,8 +1564,8 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   const __amdgpu_buffer_rsrc_t nvrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(sg.nv + (size_t)kvh * D), (short)0, new_bytes, kBufWord3);
   const float cs = prm.c;
-  uint16_t* Ks = lds[wave][0];
-  uint16_t* Vs = lds[wave][1];
+  uint16_t* Ks = kpart[wave];
+  uint16_t* Vs = vpart[wave];
 
   // K part of tile t: request u fills chunk positions 64u + lane (key
   // (64u + lane) / CPR of the tile, slot (64u + lane) % CPR) with the row's
@@ -1572,28 +1576,33 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   // (The swizzle is computed into a variable before each request: called
   // inside the builtin's argument list, the host compiler drops the kernel's
   // launch stub.)
-  auto k_issue = [&](int t) {
-    const int kt = tile_key(t);
-    const bool live = t < ntiles;
-    if (t < ncached || !live) {
+  // Cached tiles and new tiles run in two loops of their own (a wave's
+  // cached tiles all come first), each with one request pattern. In one
+  // loop with a branch per kind, the new tiles' V registers and the cached
+  // tiles' request offsets shared registers, and the compiler then waited
+  // for the K requests before every cached Vt request.
+  auto k_issue_store = [&](int t) {  // cached tile t, or nothing lands (t >= ncached)
+    const bool live = t < ncached;
 #pragma unroll
-      for (int u = 0; u < NK; ++u) {
-        const int pos = 64 * u + lane, key = pos / CPR, slot = pos % CPR;
-        const int sw = kswz<D>(key, slot) * 8;  // (a variable: see the note above)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            krsrc, (lds_void*)&Ks[512 * u], 16,
-            live ? (key * D + sw) * 2 : (int)0x80000000, live ? kt * D * 2 : 0,
-            0, 0);
-      }
-    } else {
+    for (int u = 0; u < NK; ++u) {
+      const int pos = 64 * u + lane, key = pos / CPR, slot = pos % CPR;
+      const int sw = kswz<D>(key, slot) * 8;  // (a variable: see the note above)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)&Ks[512 * u], 16,
+                                               live ? (key * D + sw) * 2 : (int)0x80000000,
+                                               live ? 32 * t * D * 2 : 0, 0, 0);
+    }
+  };
+  // (A new tile past the last re-reads the last one, unused: with an
+  // out-of-range offset chosen per tile the compiler branched around each
+  // request and lost count of them.)
+  auto k_issue_new = [&](int t) {  // new tile t (clamped to the last)
+    const int kt = tile_key(min(t, ntiles - 1));
 #pragma unroll
-      for (int u = 0; u < NK; ++u) {
-        const int pos = 64 * u + lane, key = pos / CPR, slot = pos % CPR;
-        const int sw = kswz<D>(key, slot) * 8;  // (a variable: see the note above)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            nkrsrc, (lds_void*)&Ks[512 * u], 16,
-            ((kt + key - P) * Hkv * D + sw) * 2, 0, 0, 0);
-      }
+    for (int u = 0; u < NK; ++u) {
+      const int pos = 64 * u + lane, key = pos / CPR, slot = pos % CPR;
+      const int sw = kswz<D>(key, slot) * 8;  // (a variable: see the note above)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(nkrsrc, (lds_void*)&Ks[512 * u], 16,
+                                               ((kt + key - P) * Hkv * D + sw) * 2, 0, 0, 0);
     }
   };
   // (The call's V rows are taken key-major: item (key, c) = (item % 32,
@@ -1608,24 +1617,24 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   u32x4 vreg[NK];
   const int vd = lane >> 2, vslot = lane & 3;
   const int vloc = (vd * cap + vswz4(vd, vslot) * 8) * 2;
-  auto v_issue = [&](int t) {
-    const int kt = tile_key(t);
-    if (t < ncached || t >= ntiles) {
-      const bool live = t < ntiles;
-      const int k8 = kt + 8 * vswz4(vd, vslot);
-      const int voff = live && k8 < pc ? vloc : (int)0x80000000;
+  auto v_issue_store = [&](int t) {  // cached tile t, or nothing lands (t >= ncached)
+    const bool live = t < ncached;
+    const int kt = 32 * t;
+    const int k8 = kt + 8 * vswz4(vd, vslot);
+    const int voff = live && k8 < pc ? vloc : (int)0x80000000;
 #pragma unroll
-      for (int u = 0; u < NK; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)&Vs[512 * u], 16, voff,
-                                                 live ? kt * 2 + 32 * u * cap : 0, 0, 0);
-    } else {
+    for (int u = 0; u < NK; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)&Vs[512 * u], 16, voff,
+                                               live ? kt * 2 + 32 * u * cap : 0, 0, 0);
+  };
+  auto v_issue_new = [&](int t) {  // new tile t (clamped to the last)
+    const int kt = tile_key(min(t, ntiles - 1));
 #pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        const int item = 64 * j + lane, key = item & 31, c = item >> 5;
-        vreg[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       nvrsrc, ((kt + key - P) * Hkv * D + c * 8) * 2, 0, 0));
-      }
+    for (int j = 0; j < NK; ++j) {
+      const int item = 64 * j + lane, key = item & 31, c = item >> 5;
+      vreg[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     nvrsrc, ((kt + key - P) * Hkv * D + c * 8) * 2, 0, 0));
     }
   };
   auto v_transpose = [&]() {
@@ -1739,7 +1748,13 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   };
 
   const int nmine = ntiles > wave ? (ntiles - 1 - wave) / kRowsWaves + 1 : 0;
-  k_issue(wave);
+  const int nmine_c = ncached > wave ? (ncached - 1 - wave) / kRowsWaves + 1 : 0;
+  // the first tile's K part (nothing lands for a wave with no tile) and the
+  // queries
+  if (nmine_c > 0)
+    k_issue_store(wave);
+  else if (nmine > 0)
+    k_issue_new(wave);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int pr = row0 + 16 * rt + col;
@@ -1751,30 +1766,55 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
     for (int dc = 0; dc < DC; ++dc) qreg[rt][dc] = as_bf16x8(load16(qrow + 32 * dc + 8 * kb));
   }
   // the queries and the first K part in; from here on every tile issues NK
-  // K requests after its scores and NK Vt requests after its products
+  // K requests after its scores and NK V requests after its products
   wait_vmem<0>();
-  v_issue(wave);
-  for (int j = 0; j < nmine; ++j) {
-    const int t = wave + kRowsWaves * j, kt = tile_key(t);
-    const bool cached = t < ncached;
-    wait_vmem<NK>();  // K(t) in; Vt(t) may be in flight
-    qk();
-    // (every K operand read has returned before the part is refilled)
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_sched_barrier(0);
-    k_issue(t + kRowsWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(kt, cached);
-    wait_vmem<NK>();  // Vt(t) in; K(t+8) may be in flight
-    if (!cached)
+  int j = 0;
+  // cached tiles
+  if (nmine_c > 0) {
+    v_issue_store(wave);
+    for (; j < nmine_c; ++j) {
+      const int t = wave + kRowsWaves * j, kt = 32 * t;
+      wait_vmem<NK>();  // K(t) in; Vt(t) may be in flight
+      qk();
+      // (every K operand read has returned before the part is refilled)
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_sched_barrier(0);
+      k_issue_store(t + kRowsWaves);  // (nothing lands past the cached tiles)
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(kt, true);
+      wait_vmem<NK>();  // Vt(t) in; K(t+8) may be in flight
+      if (kt + 31 >= pc) v_zero_tail(kt);
+      pv();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_sched_barrier(0);
+      v_issue_store(t + kRowsWaves);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the requests past the last cached tile landed nothing; the first new
+    // tile's K part follows
+    wait_vmem<0>();
+    if (j < nmine) k_issue_new(wave + kRowsWaves * j);
+  }
+  // new tiles (the call's rows)
+  if (j < nmine) {
+    v_issue_new(wave + kRowsWaves * j);
+    for (; j < nmine; ++j) {
+      const int t = wave + kRowsWaves * j, kt = tile_key(t);
+      wait_vmem<NK>();  // K(t) in; V(t) may be in flight
+      qk();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_sched_barrier(0);
+      k_issue_new(t + kRowsWaves);  // (past the last tile: the last re-read, unused)
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(kt, false);
+      wait_vmem<NK>();  // V(t) in; K(t+8) may be in flight
       v_transpose();
-    else if (kt + 31 >= pc)
-      v_zero_tail(kt);
-    pv();
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_sched_barrier(0);
-    v_issue(t + kRowsWaves);
-    __builtin_amdgcn_sched_barrier(0);
+      pv();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_sched_barrier(0);
+      v_issue_new(t + kRowsWaves);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // the requests for the tile past the last one: nothing lands, but they
   // must have completed before LDS is reused
@@ -1790,13 +1830,19 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
     lrun[rt] = l;
   }
   __syncthreads();  // every wave is done with its parts
-  f32x4* xo = reinterpret_cast<f32x4*>(&lds[0][0][0]);  // [wave][RT][DT][64 lanes]
+  // wave w's O: [RT][DT][64 lanes] f32x4 in the K parts (w < 4) or the Vt
+  // parts (w >= 4), RT * D * 64 bytes each (at most a quarter of an array)
+  auto xo = [&](int w) {
+    return reinterpret_cast<f32x4*>(w < kRowsWaves / 2 ? &kpart[0][0] : &vpart[0][0]) +
+           (w % (kRowsWaves / 2)) * RT * DT * 64;
+  };
+  static_assert(kRowsWaves / 2 * RT * DT * 64 * 16 <= kRowsWaves * PART * 2, "merge area");
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     wml[wave][rt][0][lane] = mref[rt];
     wml[wave][rt][1][lane] = lrun[rt];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) xo[((wave * RT + rt) * DT + dt) * 64 + lane] = O[rt][dt];
+    for (int dt = 0; dt < DT; ++dt) xo(wave)[(rt * DT + dt) * 64 + lane] = O[rt][dt];
   }
   __syncthreads();
 #pragma unroll
@@ -1819,7 +1865,7 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < kRowsWaves; ++w) {
-        const f32x4 ow = xo[((w * RT + rt) * DT + dt) * 64 + lane];
+        const f32x4 ow = xo(w)[(rt * DT + dt) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] += sw[w] * ow[i];
       }
@@ -1840,7 +1886,8 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnParams prm) {
   const int A = min(sg.row_blocks, kAppendBlocks);
   if (sg.new_tile0 >= 0 && !sg.no_append && rb < A) {
     constexpr int VST = D + 2;
-    uint16_t* Va = &lds[0][0][0];  // [64][VST]
+    uint16_t* Va = &kpart[0][0];  // [64][VST]
+    static_assert(64 * VST <= kRowsWaves * PART, "append staging area");
     uint16_t* Kw = const_cast<uint16_t*>(Kg);
     uint16_t* Vw = const_cast<uint16_t*>(Vg);
     const uint16_t* nkh = sg.nk + (size_t)kvh * D;
