@@ -632,6 +632,65 @@ def verify_sweep(backlog, layers=ROT_LAYERS, reps=3, graphs=True):
     return res
 
 
+def verify_step_graph(layers=32, copies=8, reps=3):
+    """One 9B-like layer of a verify step as a serving loop runs it: per
+    layer the QKV GEMV, the attention call over 2048 cached + m rows, then the
+    O, gate|up and down GEMVs, all layers captured in one HIP graph (each
+    layer its own KV and one of `copies` rotated weight copies), per-layer
+    time of the replay, best of `reps`. The GEMVs read fixed activation
+    buffers (the step's data flow is not modelled, only its launches and
+    bytes)."""
+    wl = synth.WORKLOADS["verify9b"]
+    hq, hkv, d, P = wl["hq"], wl["hkv"], wl["d"], wl["context"]
+    st = sve.KVSlots(1, layers, hq, hkv, d, P + 64, P)
+    st.kv_slot_select(np.arange(P + 8, dtype=np.int32))
+    c = synth.attention_case(wl["seed"], hq, hkv, d, P, 8)
+    qp, kp, vp = bf16_dev(c["q_prefix"]), bf16_dev(c["k_prefix"]), bf16_dev(c["v_prefix"])
+    for layer in range(layers):
+        st.extend_attn(0, layer, qp, kp, vp)
+    del qp, kp, vp
+    q, k, v = bf16_dev(c["q"]), bf16_dev(c["k"]), bf16_dev(c["v"])
+    g = synth.rng(3, 56)
+    shapes = synth.layer_gemv_shapes(4096, 12288, 32, 8, 128)
+    mats = []
+    for (n, kk) in shapes:
+        w, sc = synth.w4_weights(g, n, kk)
+        wd, sd = torch.from_numpy(w).cuda(), f16_dev(sc)
+        mats.append((n, kk, [sve.w4_pack(wd, sd, n, kk) for _ in range(copies)]))
+        del wd, sd
+    kmax = max(kk for _, kk in shapes)
+    x = bf16_dev(synth.normal_bf16(g, (8, kmax)))
+    res = {}
+    for m in range(1, 9):
+        qm, km, vm = q[:m].contiguous(), k[:m].contiguous(), v[:m].contiguous()
+        out = torch.empty_like(qm)
+        xs = {kk: x[:m, :kk].contiguous() for _, kk, _ in mats}
+        ys = {n: torch.empty((m, n), dtype=torch.float32, device="cuda") for n, _, _ in mats}
+
+        def gemv(i, layer):
+            n, kk, packs = mats[i]
+            sve.w4_gemv_m(xs[kk], packs[layer % copies], n, kk, ys[n])
+
+        def run():
+            for layer in range(layers):
+                gemv(0, layer)
+                st.extend_attn(0, layer, qm, km, vm, out)
+                for i in (1, 2, 3):
+                    gemv(i, layer)
+
+        gr = graph_of(run, reset=lambda: [st.kv_truncate(0, P)])
+        best = math.inf
+        for _ in range(reps):
+            st.kv_truncate(0, P)
+            with Timer() as t:
+                gr.replay()
+            best = min(best, t.ms / layers * 1e3)
+        del gr
+        res[m] = best
+    st.close()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # verify acceptance (greedy argmax over a Qwen-family vocabulary)
 # ---------------------------------------------------------------------------
@@ -912,7 +971,7 @@ def main():
                     help="time the headline from eager launches only (for counter runs)")
     ap.add_argument("--layers", type=int, default=ROT_LAYERS)
     ap.add_argument("--only", choices=["gemv", "verify", "moe", "gemm", "accept", "ceilings",
-                                       "tiny", "content", "turns"],
+                                       "tiny", "content", "turns", "verifystep"],
                     help="run one section alone and print its JSON (counter and trace runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the copy probe (256 MiB, three times): the known byte count "
@@ -942,6 +1001,7 @@ def main():
             "gemv": lambda: gemv_sweep(synth.layer_gemv_shapes(4096, 12288, 32, 8, 128), backlog,
                                        m_values=(1, 4, 8)),
             "verify": lambda: verify_sweep(backlog, layers=min(args.layers, ROT_LAYERS)),
+            "verifystep": lambda: verify_step_graph(),
             "moe": lambda: moe_sweep(backlog),
             "gemm": lambda: prefill_gemm_sweep(synth.layer_gemv_shapes(3584, 18944, 28, 4, 128),
                                                backlog),
@@ -1138,12 +1198,23 @@ def main():
         # (thinkspread's verify(m) = fixed + per-row cost, per layer here)
         step = {m: g9[m]["us"] + vs[m]["call_us"] for m in range(1, 9)}
         a4, b4 = fit(list(step), list(step.values()))
+        log("verify step graph")
+        sg = verify_step_graph()
+        a5, b5 = fit(list(sg), list(sg.values()))
         out["verify_step"] = {
             "workload": "one 9B-like layer of a verify step: the four int4 GEMVs (QKV, O, "
                         "gate|up, down) + the attention call over 2048 cached + m rows",
             "per_m_us": {m: r2(v) for m, v in step.items()},
             "fit_us": {"fixed": round(a4, 3), "per_row": round(b4, 3),
-                       "per_row_over_fixed": round(b4 / a4, 4)}}
+                       "per_row_over_fixed": round(b4 / a4, 4)},
+            "timing": "sum of the GEMV launches' HIP-event times and the attention call's "
+                      "graph-replay time",
+            "graph": {"per_m_us": {m: r2(v) for m, v in sg.items()},
+                      "fit_us": {"fixed": round(a5, 3), "per_row": round(b5, 3),
+                                 "per_row_over_fixed": round(b5 / a5, 4)},
+                      "timing": "32 layers, each QKV GEMV, attention, O, gate|up and down "
+                                "captured in one HIP graph and replayed (rotated weight "
+                                "copies), per layer"}}
         log("verify accept")
         va = verify_accept_sweep(backlog)
         out["verify_accept"] = {
