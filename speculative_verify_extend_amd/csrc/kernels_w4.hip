@@ -499,10 +499,18 @@ struct LongBuf {
 };
 
 constexpr int kLongMaxWaves = 8;
+constexpr int kLongDepth = 2;  // steps in flight per wave (3: 9.0 us, 4: 11.1 us against 8.8 at m = 1)
 
+// NU = (m + 1) / 2 compact activation loads per step, a template argument:
+// with a count known only at run time the compiler could not count the
+// step's requests, and before each step's products it waited for the
+// oldest requests of the next step as well (one step in flight, not two).
+// (x, nib and scl are not declared __restrict__: with it the compiler may
+// move their loads across the fences below.)
+template <int NU>
 __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
-    const uint16_t* __restrict__ x, int m, const uint8_t* __restrict__ nib,
-    const uint8_t* __restrict__ scl, int N, int K, int Q, int n_tiles, float* __restrict__ y) {
+    const uint16_t* x, int m, const uint8_t* nib, const uint8_t* scl, int N, int K, int Q,
+    int n_tiles, float* __restrict__ y) {
   __shared__ f32x4 part[kGemvMaxWaves * 64];
   // per wave: one step's activations, [row][kLongStepK] bf16 with rows
   // kXRow elements apart, rewritten every step (LDS operations of a wave
@@ -520,7 +528,9 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
   const int q0 = wave * per;
   const int nq = max(0, min(per, Q - q0));
   const int nchunks = (per + kLongChunk - 1) / kLongChunk;  // same for every wave
-  const int nu = (m + 1) / 2;  // compact activation loads per step (2 rows each)
+  // (m <= 16, K < 2^26: the byte offsets fit 32 bits)
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, m * K * 2, kBufWord3);
   const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t loff = lane * 16, soff = r * 8;
@@ -539,14 +549,16 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
     // lanes kb < 2 fetch quad 0's scale row, lanes kb >= 2 quad 1's
     b.s[0] = *reinterpret_cast<const u32x2*>(scl + (tbase + quad_of(c, kb >> 1)) * 128 + soff);
     // compact activations: lane slot e = lane + 64u holds row e / 32,
-    // elements 8 * (e % 32) .. +7 of the step (quad (e % 32) / 16)
+    // elements 8 * (e % 32) .. +7 of the step (quad (e % 32) / 16); a row
+    // past m (the second row of the last load when m is odd) reads past the
+    // buffer's end: zeros, no fetch, and the request count stays NU
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < nu) {  // uniform
-        const int e = lane + 64 * u, rr = e >> 5, kc = e & 31;
-        const int k = min(128 * quad_of(c, kc >> 4) + 8 * (kc & 15), K - 8);
-        if (rr < m) b.xc[u] = load16(x + (size_t)rr * K + k);  // no write on the other side
-      }
+    for (int u = 0; u < NU; ++u) {
+      const int e = lane + 64 * u, rr = e >> 5, kc = e & 31;
+      const int k = min(128 * quad_of(c, kc >> 4) + 8 * (kc & 15), K - 8);
+      b.xc[u] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     xrs, rr < m ? (uint32_t)(rr * K + k) * 2u : 0x80000000u, 0, 0));
     }
   };
   f32x4 acc = zero4;
@@ -558,11 +570,10 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
       b.s[1][e] = __shfl(own[e], r + 32, 64);  // a lane with kb = 2
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < nu) {
-        const int e = lane + 64 * u;  // row e / 32, elements 8 * (e % 32) .. +7
-        store16(xw + (e >> 5) * kXRow + 8 * (e & 31), b.xc[u]);
-      }
+    for (int u = 0; u < NU; ++u) {
+      const int e = lane + 64 * u;  // row e / 32, elements 8 * (e % 32) .. +7
+      store16(xw + (e >> 5) * kXRow + 8 * (e & 31), b.xc[u]);
+    }
 #pragma unroll
     for (int a = 0; a < kLongChunk; ++a) {
       const bool real = c * kLongChunk + a < nq;  // uniform
@@ -576,21 +587,35 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
       }
     }
   };
-  LongBuf A, B;
-  issue(0, A);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(1, B);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int c = 0; c < nchunks; c += 2) {
-    consume(c, A);
+  // kLongDepth steps in flight. The first round is peeled, so the loop is
+  // entered with the request history of its own back edge (the prologue's
+  // requests came out interleaved, and at a merged loop head the compiler
+  // then waited for the next step's requests too). Steps past nchunks are
+  // clamped re-reads with scale 0.
+  // (The fences also stop loads from being moved at the IR level, where a
+  // scheduling barrier does not hold: an activation load sunk below the
+  // next step's requests changed the order the waits count on.)
+  auto fence = [] {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue(c + 2, A);
-    __builtin_amdgcn_sched_barrier(0);
-    consume(c + 1, B);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(c + 3, B);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  LongBuf buf[kLongDepth];
+#pragma unroll
+  for (int d = 0; d < kLongDepth; ++d) {
+    issue(d, buf[d]);
+    fence();
   }
+  auto round = [&](int c) {
+#pragma unroll
+    for (int d = 0; d < kLongDepth; ++d) {
+      consume(c + d, buf[d]);
+      fence();
+      issue(c + d + kLongDepth, buf[d]);
+      fence();
+    }
+  };
+  round(0);
+  for (int c = kLongDepth; c < nchunks; c += kLongDepth) round(c);
   park(part, wave, acc);
   flush_tiles(part, W, tile, 1, m, N, y);
 }
@@ -790,15 +815,18 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
       const uint32_t xoff =
           r < cnt ? (uint32_t)(((x_per_slot ? (size_t)pr : (size_t)(pr / topk)) * K + 8 * kb) * 2)
                   : 0x80000000u;
+      // (unconditional loads, quads past K reading past the buffer's end:
+      // a load under a condition made the compiler lose count of the
+      // requests and wait for all of them in the tile loop)
       bf16x8 xa[QPW][4];
 #pragma unroll
       for (int a = 0; a < QPW; ++a)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          xa[a][j] = a < nq ? as_bf16x8(__builtin_bit_cast(
-                                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             xrs, xoff + 64u * min(4 * (q0 + a) + j, G - 1), 0, 0)))
-                            : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+          xa[a][j] = as_bf16x8(__builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         xrs, a < nq ? xoff + 64u * min(4 * (q0 + a) + j, G - 1) : 0x80000000u,
+                         0, 0)));
       auto consume = [&](const TileBuf<QPW>& b) {
         f32x4 acc = zero4;
 #pragma unroll
@@ -826,7 +854,12 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
         __syncthreads();
       };
       // double-buffered walk over the run (as in the dense short kernel);
-      // tiles t0 and t0+1 are already requested
+      // tiles t0 and t0+1 are already requested. Everything requested so
+      // far is awaited here (the activations were requested after both
+      // tiles, so the first products need all of it anyway): the loop head
+      // otherwise merges two different counts of loads in flight and the
+      // compiler then waits for all of them in every step.
+      wait_vmem<0>();
       int tb = t0;
       for (int t = t0; t < t1; t += 2) {
         const f32x4 acc0 = consume(A);
@@ -838,7 +871,11 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
         __builtin_amdgcn_sched_barrier(0);
         issue(t + 3, B);
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 1 < t1) park(part, (t + 1 - tb) * W + wave, acc1);
+        // parked even past the run's end (an odd run): the slot is inside
+        // the batch (t - tb + 2 <= batch, batch even) and never summed, and
+        // a store under a condition let the compiler finish acc1 after the
+        // next requests, which then waited for them
+        park(part, (t + 1 - tb) * W + wave, acc1);
         const int done = min(t + 2, t1) - tb;
         if (done + 2 > batch || t + 2 >= t1) {
           flush(tb, done);
@@ -1438,8 +1475,20 @@ hipError_t launch_w4_gemv(const void* x, int m, const void* packed, int N, int K
 #undef SVE_SHORT
   } else {
     const int W = kLongMaxWaves;
-    hipLaunchKernelGGL(w4_gemv_long_kernel, dim3(n_tiles), dim3(64 * W), 0, st, xp, m, nib, scl, N,
-                       K, Q, n_tiles, y);
+#define SVE_LONG(NU_)                                                                            \
+  hipLaunchKernelGGL(w4_gemv_long_kernel<NU_>, dim3(n_tiles), dim3(64 * W), 0, st, xp, m, nib, scl, \
+                     N, K, Q, n_tiles, y)
+    switch ((m + 1) / 2) {
+      case 1: SVE_LONG(1); break;
+      case 2: SVE_LONG(2); break;
+      case 3: SVE_LONG(3); break;
+      case 4: SVE_LONG(4); break;
+      case 5: SVE_LONG(5); break;
+      case 6: SVE_LONG(6); break;
+      case 7: SVE_LONG(7); break;
+      default: SVE_LONG(8); break;
+    }
+#undef SVE_LONG
   }
   return hipGetLastError();
 }
