@@ -57,7 +57,9 @@ typedef struct {
   int32_t head_dim;   /* D: 64 or 128 */
   int32_t capacity;   /* max tokens per slot (rounded up to a multiple of 64) */
   int32_t max_rows;   /* max new rows per extend call (sum over a batched call),
-                         1..4*capacity; sizes the split workspace */
+                         1..4*capacity, and max_rows * n_q_heads * head_dim * 2
+                         below 2 GiB (one key split's partials); sizes the
+                         split workspace */
   int32_t reuse;      /* 0: select always reports 0 reused tokens */
   int32_t match_rule; /* 0: lone-slot clause on (default); 1: literal rule */
 } sve_config;

@@ -47,6 +47,8 @@ bool config_ok(const sve_config* c, std::string* why) {
   if (c->capacity < 1 || c->capacity > (1 << 20)) return *why = "capacity out of range", false;
   if (c->max_rows < 1 || c->max_rows > SVE_MAX_SLOTS * c->capacity)
     return *why = "max_rows must be 1..4*capacity", false;
+  if ((size_t)c->max_rows * c->n_q_heads * c->head_dim * 2 >= ((size_t)1 << 31))
+    return *why = "max_rows * n_q_heads * head_dim * 2 must stay below 2 GiB", false;
   if (c->match_rule != 0 && c->match_rule != 1) return *why = "match_rule must be 0 or 1", false;
   return true;
 }

@@ -61,6 +61,12 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) {
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBufWord3 = 0x00020000;
 
+// Cache policy of a buffer store that writes through this XCD's L2 (the
+// sc1 bit: device scope). Split partials leave this way: the kernel that
+// adds them runs on every XCD and finds them in memory, instead of dirty in
+// the writer's L2 until that kernel's end writes the L2 back.
+constexpr int kStoreThrough = 16;
+
 // wait until at most N vector-memory requests of this wave are outstanding
 // (lgkm and export counters untouched)
 template <int N>

@@ -712,12 +712,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       }
     } else {
       const float f = ldexpf(inv, -ex);
-      const size_t wrow = ((size_t)split * m * Hq) * D + orow;
       // The row's fp16 partial goes through this wave's own LDS rows (group
       // 1's second buffer, unused after the merge; LDS operations of a wave
       // complete in order), so that each lane stores 16 contiguous bytes and
-      // a row leaves as 64-byte runs rather than 8-byte pieces. Streaming
-      // stores: the partials are read once, by the combine kernel.
+      // a row leaves as 64-byte runs rather than 8-byte pieces. The stores
+      // write through the L2 (read once, by the combine kernel, from any
+      // XCD). Buffer resources over this split's partials (the host keeps
+      // one split's partials below 2 GiB).
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+          sg.ws_o + (size_t)split * m * Hq * D, (short)0, m * Hq * D * 2, kBufWord3);
+      const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+          sg.ws_ml + (size_t)split * m * Hq * 4, (short)0, m * Hq * 16, kBufWord3);
       uint32_t* sr = reinterpret_cast<uint32_t*>(&lds[1][1][0][0]) + (gw * 16 + col) * kStageRow<D>;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -728,12 +733,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnParams prm) {
       }
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sr + 16 * c + 4 * kb),
-                                    reinterpret_cast<u32x4*>(sg.ws_o + wrow + 32 * c + 8 * kb));
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sr + 16 * c + 4 * kb),
+                                               ors, (uint32_t)((orow + 32 * c + 8 * kb) * 2), 0,
+                                               kStoreThrough);
       if (kb == 0)
-        __builtin_nontemporal_store(
-            f32x4{mref[rt], l, ldexpf(1.f, ex), 0.f},
-            reinterpret_cast<f32x4*>(sg.ws_ml + (((size_t)split * m + qi) * Hq + qh) * 4));
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, f32x4{mref[rt], l, ldexpf(1.f, ex), 0.f}), mrs,
+            (uint32_t)(((size_t)qi * Hq + qh) * 16), 0, kStoreThrough);
     }
   }
 }

@@ -39,7 +39,8 @@ def test_arena_bytes_layout(lib):
 
 @pytest.mark.parametrize("bad", [dict(n_slots=0), dict(n_slots=5), dict(head_dim=96),
                                  dict(n_q_heads=30), dict(max_rows=0), dict(max_rows=9000),
-                                 dict(n_layers=0), dict(match_rule=2)])
+                                 dict(n_layers=0), dict(match_rule=2),
+                                 dict(capacity=1 << 20, max_rows=1 << 20)])
 def test_bad_configs_are_rejected(lib, bad):
     c = _cfg(**bad)
     assert lib.sve_arena_bytes(C.byref(c), 1) == 0
