@@ -38,6 +38,11 @@ COMMON_FLAGS = [
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # kernel arguments of scalar and pointer type start out in scalar
+    # registers (the first 16 dwords), so a kernel's first loads do not wait
+    # for a load of its argument block; kernels taking one parameter struct
+    # by value are not eligible and load it as before
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
