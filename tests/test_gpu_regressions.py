@@ -11,6 +11,10 @@ against the fp64 oracle through the C ABI:
   question and when the questions run past the slot's capacity.
 - a batched call of decode-sized pieces with few KV heads plans its key
   splits within the split workspace (the slot rows after it stay intact).
+
+And one guard for the split partials, which leave the attention kernel by
+stores that write through the L2: consecutive split calls on one context,
+each over the same workspace, read only their own partials.
 """
 import numpy as np
 import pytest
@@ -152,3 +156,33 @@ def test_batched_decode_pieces_fit_the_split_workspace():
         kk, vv = st.kv_read(s, 0, 0, P + m)
         assert np.array_equal(host_bits(kk), np.concatenate([c["k_prefix"], c["k"]]))
         assert np.array_equal(host_bits(vv), np.concatenate([c["v_prefix"], c["v"]]))
+
+
+@pytest.mark.parametrize("path", ["mfma-split5", "mfma-balanced", "decode-split3"])
+def test_consecutive_split_calls_read_only_their_own_partials(path):
+    """One slot holding 1668 rows; six extends in a row, each cut back to
+    the same 1668 rows first, with fresh q/k/v of alternating sizes (254,
+    37, 254, 8, 254, 3 rows on the MFMA path; 8, 3, 8, 1, 8, 5 on the decode
+    path), every one on a split layout over the same workspace. Each output
+    matches the oracle of its own inputs: no call's combine reads a partial
+    of an earlier call."""
+    hq, hkv, d, P = 28, 4, 128, 1668
+    env_of = {"mfma-split5": dict(SVE_MFMA_MIN_ROWS=1, SVE_KV_SPLIT=5),
+              "mfma-balanced": dict(SVE_MFMA_MIN_ROWS=1, SVE_ATTN_LAYOUT=3),
+              "decode-split3": dict(SVE_ATTN_PATH="decode", SVE_KV_SPLIT=3)}[path]
+    ms = [8, 3, 8, 1, 8, 5] if path.startswith("decode") else [254, 37, 254, 8, 254, 3]
+    announce(f"consecutive split calls path={path}")
+    base = synth.attention_case(500, hq, hkv, d, P, 0)
+    st = sve.KVSlots(1, 1, hq, hkv, d, P + 256 + 64, P)
+    assert st.kv_slot_select(np.arange(P + 256, dtype=np.int32)) == (0, 0)
+    st.extend_attn(0, 0, dev_bf16(base["q_prefix"]), dev_bf16(base["k_prefix"]),
+                   dev_bf16(base["v_prefix"]))
+    for i, m in enumerate(ms):
+        st.kv_truncate(0, P)
+        c = synth.attention_case(600 + i, hq, hkv, d, 0, m)
+        with env(**env_of):
+            out = st.extend_attn(0, 0, dev_bf16(c["q"]), dev_bf16(c["k"]), dev_bf16(c["v"]))
+        got = host_f64_of_bf16(out)
+        want = extend_attention(c["q"], np.concatenate([base["k_prefix"], c["k"]]),
+                                np.concatenate([base["v_prefix"], c["v"]]), P)
+        assert np.abs(got - want).max() <= ATTN_TOL, (i, m)
