@@ -409,19 +409,31 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kerne
   };
 
   const uint32_t loff = lane * 16, soff = r * 8;
+  // Requests through buffer resources over one tile's blocks. A request
+  // past the run gets a resource of no bytes: every lane reads past its end
+  // (zeros, no fetch), while the instructions and their count stay the
+  // same (its sums are parked in slots the flush does not read). Re-reading
+  // the run's last tile instead cost each workgroup two tiles of load
+  // bandwidth at the end of a run of two.
   auto issue = [&](int i, TileBuf<QPW>& b) {
     const int t = t0 + min(i, cnt - 1) * ts;
+    const bool live = i < cnt;  // (uniform)
+    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(nib + (size_t)t * Q * 1024), (short)0, live ? Q * 1024 : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scl + (size_t)t * Q * 128), (short)0, live ? Q * 128 : 0, kBufWord3);
 #pragma unroll
     for (int a = 0; a < QPW; ++a) {
-      const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
-      b.w[a] = load16(nib + blk * 1024 + loff);
-      if constexpr (QPW != 2) b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+      const uint32_t q = min(q0 + a, Q - 1);
+      b.w[a] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nrs, q * 1024 + loff, 0, 0));
+      if constexpr (QPW != 2)
+        b.s[a] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, q * 128 + soff, 0, 0));
     }
     if constexpr (QPW == 2) {
       // one scale load for both quads: lanes kb < 2 fetch quad 0's row,
       // lanes kb >= 2 quad 1's (spread to every lane when consumed)
-      const size_t blk = (size_t)t * Q + min(q0 + (kb >> 1), Q - 1);
-      b.s[0] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+      const uint32_t q = min(q0 + (kb >> 1), Q - 1);
+      b.s[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, q * 128 + soff, 0, 0));
     }
   };
   auto consume = [&](TileBuf<QPW> b) {
@@ -528,9 +540,7 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
   const int q0 = wave * per;
   const int nq = max(0, min(per, Q - q0));
   const int nchunks = (per + kLongChunk - 1) / kLongChunk;  // same for every wave
-  // (m <= 16, K < 2^26: the byte offsets fit 32 bits)
-  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(x), (short)0, m * K * 2, kBufWord3);
+  // (m <= 16, K < 2^26: the activation byte offsets fit 32 bits)
   const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t loff = lane * 16, soff = r * 8;
@@ -540,14 +550,23 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
 
   auto quad_of = [&](int c, int a) { return min(q0 + min(c * kLongChunk + a, max(nq - 1, 0)), Q - 1); };
   static_assert(kLongChunk == 2, "one scale load serves the two quads of a step");
+  // A step past the wave's last one (the pipeline's tail) requests through
+  // resources of no bytes: zeros, no fetch, the same instructions.
   auto issue = [&](int c, LongBuf& b) {
+    const bool live = c < nchunks;  // (uniform)
+    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(nib + tbase * 1024), (short)0, live ? Q * 1024 : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scl + tbase * 128), (short)0, live ? Q * 128 : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t xcs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), (short)0, live ? m * K * 2 : 0, kBufWord3);
 #pragma unroll
-    for (int a = 0; a < kLongChunk; ++a) {
-      const size_t blk = tbase + quad_of(c, a);
-      b.w[a] = load16(nib + blk * 1024 + loff);
-    }
+    for (int a = 0; a < kLongChunk; ++a)
+      b.w[a] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             nrs, (uint32_t)quad_of(c, a) * 1024 + loff, 0, 0));
     // lanes kb < 2 fetch quad 0's scale row, lanes kb >= 2 quad 1's
-    b.s[0] = *reinterpret_cast<const u32x2*>(scl + (tbase + quad_of(c, kb >> 1)) * 128 + soff);
+    b.s[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                           srs, (uint32_t)quad_of(c, kb >> 1) * 128 + soff, 0, 0));
     // compact activations: lane slot e = lane + 64u holds row e / 32,
     // elements 8 * (e % 32) .. +7 of the step (quad (e % 32) / 16); a row
     // past m (the second row of the last load when m is odd) reads past the
@@ -558,7 +577,7 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
       const int k = min(128 * quad_of(c, kc >> 4) + 8 * (kc & 15), K - 8);
       b.xc[u] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     xrs, rr < m ? (uint32_t)(rr * K + k) * 2u : 0x80000000u, 0, 0));
+                     xcs, rr < m ? (uint32_t)(rr * K + k) * 2u : 0x80000000u, 0, 0));
     }
   };
   f32x4 acc = zero4;
@@ -590,8 +609,8 @@ __global__ __launch_bounds__(64 * kLongMaxWaves) void w4_gemv_long_kernel(
   // kLongDepth steps in flight. The first round is peeled, so the loop is
   // entered with the request history of its own back edge (the prologue's
   // requests came out interleaved, and at a merged loop head the compiler
-  // then waited for the next step's requests too). Steps past nchunks are
-  // clamped re-reads with scale 0.
+  // then waited for the next step's requests too). Steps past nchunks
+  // request nothing (empty resources) and add zero.
   // (The fences also stop loads from being moved at the IR level, where a
   // scheduling barrier does not hold: an activation load sunk below the
   // next step's requests changed the order the waits count on.)
@@ -754,13 +773,20 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_routed_shor
   const bf16x8 neg136 = neg136_operand();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t loff = lane * 16, soff = r * 8;
+  // (a tile past the run requests through resources of no bytes: zeros,
+  // no fetch, the same instructions)
   auto issue = [&](int t, TileBuf<QPW>& b) {
+    const bool live = t < t1;  // (uniform)
     t = min(t, t1 - 1);
+    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(nib + (size_t)t * Q * 1024), (short)0, live ? Q * 1024 : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scl + (size_t)t * Q * 128), (short)0, live ? Q * 128 : 0, kBufWord3);
 #pragma unroll
     for (int a = 0; a < QPW; ++a) {
-      const size_t blk = (size_t)t * Q + min(q0 + a, Q - 1);
-      b.w[a] = load16(nib + blk * 1024 + loff);
-      b.s[a] = *reinterpret_cast<const u32x2*>(scl + blk * 128 + soff);
+      const uint32_t q = min(q0 + a, Q - 1);
+      b.w[a] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nrs, q * 1024 + loff, 0, 0));
+      b.s[a] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, q * 128 + soff, 0, 0));
     }
   };
   // the first pass's first two tiles (an invalid expert id reads expert 0's,
