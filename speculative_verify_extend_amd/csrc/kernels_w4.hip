@@ -271,9 +271,10 @@ __host__ __device__ inline int gemv_ks(int Q) { return Q >= 8 ? 8 : Q >= 4 ? 4 :
 //  * long K: one tile per workgroup; each wave walks its slice two quads at
 //    a time with weights, scales and activations double buffered, C0 being
 //    computed per group.
-// Loads past the end of a run or slice re-read the last valid block (an L2
-// hit) so that no load sits under a data-dependent branch; their results
-// are discarded or scaled by zero.
+// No load sits under a data-dependent branch: requests past the end of a
+// run (or of a wave's slice) keep their instructions, reading either
+// through a buffer resource of no bytes (zeros, no fetch) or, inside a
+// slice, the last valid block; their results are discarded or add zero.
 // ---------------------------------------------------------------------------
 
 constexpr int kGemvMaxWaves = 16;
@@ -467,8 +468,8 @@ __global__ __launch_bounds__(64 * short_max_waves(QPW)) void w4_gemv_short_kerne
   }
   // walk over the run with PD tiles in flight; the fences keep each
   // buffer's loads contiguous in issue order so the wait before a consume
-  // covers only it. Requests past the run re-read its last tile, and their
-  // sums are parked in slots the flush does not read (a flush comes before
+  // covers only it. Requests past the run fetch nothing (see issue), and
+  // their sums are parked in slots the flush does not read (a flush comes before
   // a batch could hold more than `batch` tiles; a conditional park here
   // split the schedule and spilled).
   TileBuf<QPW> buf[PD];
