@@ -85,6 +85,24 @@ def test_gemv_strided_and_contiguous_runs_agree(n, k, monkeypatch):
     assert err.max() <= GEMV_TOL, err
 
 
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("k", [9088, 10240])
+def test_gemv_long_k_ragged_slices(k, m):
+    """Long K with an odd number of two-quad steps per wave (10240: 80 quads,
+    10 per wave) and a short last wave (9088: 71 quads, 9 per wave, the last
+    wave 8): the pipeline's tail steps fetch nothing and add zero; sampled
+    rows match the oracle."""
+    n = 1000
+    announce(f"gemv long k={k} m={m}")
+    w, s, packed = _weights(12, n, k)
+    xh = synth.normal_bf16(synth.rng(13, k, m), (m, k))
+    y = sve.w4_gemv_m(dev_bf16(xh), packed, n, k).cpu().numpy()
+    cols = np.unique(np.concatenate([np.arange(0, n, 7), np.arange(n - 16, n)]))
+    want = ow4.gemv(xh, w[cols], s[cols], k)
+    err = rel_l2_rows(y[:, cols], want)
+    assert err.max() <= GEMV_TOL, err
+
+
 def test_gemv_one_hot_is_exact():
     """x = e_c reads column c of the dequantised matrix exactly."""
     n, k = 300, 512
